@@ -1,0 +1,285 @@
+"""Benchmark of the fine-grained FP8 hot path on one MI355X.
+
+A step is one pass of the dense Fprop path on the 4096 x 7168 x 4096 workload
+(DeepSeek-V3 hidden size 7168): 1x128 quantization of the activation
+A [4096][7168] (BF16 -> E4M3 + FP32 scales), 128x128 block quantization of
+the weight W [7168][4096], and the block-scaled FP8 GEMM producing FP32
+C [4096][4096].  Inputs are seeded synthetic tensors already resident in HBM;
+the step rotates over several input/output sets whose total exceeds the
+256 MB Infinity Cache, so reads come from HBM.
+
+`value` = 2*M*N*K / step time (TFLOP/s of the whole step, quantizers
+included).  `roofline` reports the GEMM kernel alone (average duration from
+HIP events around each launch in the timed region) against the dense FP8
+MFMA peak.  `kernels` adds each kernel's time and roofline fraction, and
+`extras` times the other workloads' kernels (backward Dgrad/Wgrad, the
+accumulation study, the MoE grouped GEMMs).  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published (no sparsity)
+QUANT_BYTES_1X128 = 2 + 1 + 4 / 128       # per element: BF16 read, code write, scale per 128
+QUANT_BYTES_BLOCK = 2 + 1 + 4 / (128 * 128)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def timed_events(torch, fn, reps):
+    """Average duration (ms) of fn() over reps launches, HIP events on the
+    current stream around each launch."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is "
+              "described, not built.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fp8_fine_grained_quantize_amd as fb
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    M, K, N = 4096, 7168, 4096
+    A0, W0 = synthetic.dense_fprop()
+    S = args.sets
+    A = [A0.to(dev)] + [torch.roll(A0, shifts=i, dims=0).to(dev) for i in range(1, S)]
+    W = [W0.to(dev)] + [torch.roll(W0, shifts=i, dims=1).to(dev) for i in range(1, S)]
+    qA = [torch.empty(M, K, dtype=torch.uint8, device=dev) for _ in range(S)]
+    sA = [torch.empty(K // 128, M, dtype=torch.float32, device=dev) for _ in range(S)]
+    qW = [torch.empty(K, N, dtype=torch.uint8, device=dev) for _ in range(S)]
+    sW = [torch.empty(K // 128, N // 128, dtype=torch.float32, device=dev) for _ in range(S)]
+    C = [torch.empty(M, N, dtype=torch.float32, device=dev) for _ in range(S)]
+
+    ev = {k: [] for k in ("q1x128", "qblock", "gemm")}
+
+    def step(i, record=False):
+        j = i % S
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record()
+        fb.quantize_1x128(A[j], q=qA[j], s=sA[j])
+        if record:
+            e[1].record()
+        fb.quantize_block128(W[j], q=qW[j], s=sW[j])
+        if record:
+            e[2].record()
+        fb.gemm_fp8_blockscaled(qA[j], sA[j], qW[j], sW[j], opB=fb.OP_N, bscale_mode=fb.BSCALE_BLOCK128, C=C[j])
+        if record:
+            e[3].record()
+            ev["q1x128"].append((e[0], e[1]))
+            ev["qblock"].append((e[1], e[2]))
+            ev["gemm"].append((e[2], e[3]))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, synchronized on both sides.
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i, record=True)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    def avg(k):
+        return sum(a.elapsed_time(b) for a, b in ev[k]) / len(ev[k])
+
+    t_q1, t_qb, t_g = avg("q1x128"), avg("qblock"), avg("gemm")
+    gemm_tflops = flops / (t_g * 1e-3) / 1e12
+    q1_gbs = M * K * QUANT_BYTES_1X128 / (t_q1 * 1e-3) / 1e9
+    qb_gbs = K * N * QUANT_BYTES_BLOCK / (t_qb * 1e-3) / 1e9
+    kernels = {
+        "quantize_1x128": {"us": round(t_q1 * 1e3, 2), "GB/s": round(q1_gbs, 1), "frac_hbm": round(q1_gbs / HBM_PEAK_GBS, 4)},
+        "quantize_block128": {"us": round(t_qb * 1e3, 2), "GB/s": round(qb_gbs, 1), "frac_hbm": round(qb_gbs / HBM_PEAK_GBS, 4)},
+        "gemm_fp8_blockscaled": {"us": round(t_g * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
+                                 "frac_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4)},
+    }
+
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(torch, fb, synthetic, dev, np)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(np, synthetic, A0, W0, M, N, K)
+
+    out = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) activations with 1% outlier channels x30, N(0,0.006) weights)",
+        "config": {"workload": "dense Fprop: q1x128(A[4096][7168]) + q128x128(W[7168][4096]) + FP8 GEMM 4096x4096x7168, FP32 out",
+                   "M": M, "N": N, "K": K, "rotating_sets": S, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_fp8_blockscaled", "algorithmic": "2*M*N*K = 240.52 GFLOP per launch"},
+        "kernels": kernels,
+        "extras": extras,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+def run_extras(torch, fb, synthetic, dev, np):
+    """Per-kernel timings on the other workloads (HIP events, few reps)."""
+    res = {}
+    reps = 10
+    # backward: Dgrad dX = dY W^T (OP_T), Wgrad dW = X^T dY (128x1 operands, ROW128)
+    X, W, dY = synthetic.backward()
+    Xd, Wd, dYd = X.to(dev), W.to(dev), dY.to(dev)
+    qdY, sdY = fb.quantize_1x128(dYd)
+    qW, sW = fb.quantize_block128(Wd)
+    qXT, sXT = fb.quantize_128x1(Xd)
+    qdYT, sdYT = fb.quantize_128x1(dYd)
+    torch.cuda.synchronize()
+    Cd = torch.empty(4096, 7168, dtype=torch.float32, device=dev)
+    Cw = torch.empty(7168, 2048, dtype=torch.float32, device=dev)
+    fl = 2.0 * 4096 * 7168 * 2048
+    t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qdY, sdY, qW, sW, opB=fb.OP_T, C=Cd), reps)
+    res["dgrad_4096x7168x2048"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(fl / t / 1e9, 1)}
+    t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qXT, sXT, qdYT, sdYT, opB=fb.OP_T,
+                                                              bscale_mode=fb.BSCALE_ROW128, C=Cw), reps)
+    res["wgrad_7168x2048x4096"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(fl / t / 1e9, 1)}
+    for name, x, fn, bpe in [("quantize_128x1_X", Xd, fb.quantize_128x1, QUANT_BYTES_1X128),
+                             ("quantize_128x1_dY", dYd, fb.quantize_128x1, QUANT_BYTES_1X128),
+                             ("quantize_1x128_dY", dYd, fb.quantize_1x128, QUANT_BYTES_1X128)]:
+        qo, so = fn(x)
+        t = timed_events(torch, lambda i: fn(x, q=qo, s=so) if fn is not fb.quantize_128x1 else fn(x, qT=qo, s=so), reps)
+        gbs = x.numel() * bpe / (t * 1e-3) / 1e9
+        res[name] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    qT2, sT2 = fb.requantize_128x1_from_1x128(qdY, sdY)
+    t = timed_events(torch, lambda i: fb.requantize_128x1_from_1x128(qdY, sdY, qT=qT2, sT=sT2), reps)
+    gbs = dY.numel() * (1 + 1 + 8 / 128) / (t * 1e-3) / 1e9
+    res["requantize_128x1_from_1x128_dY"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1),
+                                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    del Xd, Wd, dYd, qXT, qdYT, Cd, Cw
+    # accumulation study shapes
+    for Kc in (4096, 8192, 16384):
+        a, b = synthetic.accum_study(Kc)
+        qa, sa = fb.quantize_1x128(a.to(dev))
+        qb, sb = fb.quantize_block128(b.to(dev))
+        c = torch.empty(1024, 1024, dtype=torch.float32, device=dev)
+        t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qa, sa, qb, sb, C=c), reps)
+        res[f"gemm_1024x1024x{Kc}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(2.0 * 1024 * 1024 * Kc / t / 1e9, 1)}
+    torch.cuda.empty_cache()
+    # MoE grouped up/gate and down projections (256 experts, top-8 of 8192 tokens)
+    r = synthetic.moe_routing()
+    X8 = r["X"].to(dev)
+    tok = r["token_of_row"].to(dev)
+    offs = r["offsets"].to(torch.int32).to(dev)
+    G, Kh, Nu, Nd = 256, 7168, 4096, 7168
+    qX, sX = fb.quantize_1x128(X8, pow2=True)
+    t = timed_events(torch, lambda i: fb.quantize_1x128(X8, pow2=True, q=qX, s=sX), reps)
+    gbs = X8.numel() * QUANT_BYTES_1X128 / (t * 1e-3) / 1e9
+    res["quantize_1x128_pow2_moe_X"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    qA = qX[tok].contiguous()
+    sA = sX[:, tok].contiguous()
+    Mt = qA.shape[0]
+    qU = torch.empty(G, Kh, Nu, dtype=torch.uint8, device=dev)
+    sU = torch.empty(G, Kh // 128, Nu // 128, dtype=torch.float32, device=dev)
+    for e in range(G):
+        fb.quantize_block128(synthetic.expert_weight("up", e, device=dev), q=qU[e], s=sU[e])
+    Cu = torch.empty(Mt, Nu, dtype=torch.float32, device=dev)
+    t = timed_events(torch, lambda i: fb.grouped_gemm_fp8_blockscaled(offs, qA, sA, qU, sU, C=Cu), 3)
+    fl = 2.0 * Mt * Nu * Kh
+    byts = G * Kh * Nu + Mt * Kh + Mt * Nu * 4
+    res["grouped_up_gate_65536x4096x7168_E256"] = {"us": round(t * 1e3, 1), "TFLOP/s": round(fl / t / 1e9, 1),
+                                                    "GB/s": round(byts / t / 1e6, 1),
+                                                    "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4),
+                                                    "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
+    del qU, sU
+    torch.cuda.empty_cache()
+    H = (torch.nn.functional.silu(Cu[:, :2048]) * Cu[:, 2048:]).to(torch.bfloat16)
+    del Cu
+    qH, sH = fb.quantize_1x128(H)
+    qD = torch.empty(G, 2048, Nd, dtype=torch.uint8, device=dev)
+    sD = torch.empty(G, 2048 // 128, Nd // 128, dtype=torch.float32, device=dev)
+    for e in range(G):
+        fb.quantize_block128(synthetic.expert_weight("down", e, device=dev), q=qD[e], s=sD[e])
+    Cdn = torch.empty(Mt, Nd, dtype=torch.float32, device=dev)
+    t = timed_events(torch, lambda i: fb.grouped_gemm_fp8_blockscaled(offs, qH, sH, qD, sD, C=Cdn), 3)
+    fl = 2.0 * Mt * Nd * 2048
+    byts = G * 2048 * Nd + Mt * 2048 + Mt * Nd * 4
+    res["grouped_down_65536x7168x2048_E256"] = {"us": round(t * 1e3, 1), "TFLOP/s": round(fl / t / 1e9, 1),
+                                                 "GB/s": round(byts / t / 1e6, 1),
+                                                 "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4),
+                                                 "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
+    return res
+
+
+def cpu_baseline(np, synthetic, A0, W0, M, N, K):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    step: 1x128 quantization of the first 512 rows of A, block quantization
+    of all of W, and the GEMM for those 512 rows (all 4096 columns).  Scaled
+    to TFLOP/s of the GEMM FLOPs covered by the sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    rows = 512
+    a_bits = synthetic.bf16_bits(A0[:rows])
+    w_bits = synthetic.bf16_bits(W0)
+    t0 = time.perf_counter()
+    qa, sa = oracle.quantize_1x128(a_bits)
+    qw, sw = oracle.quantize_block128(w_bits)
+    oracle.gemm_blockscaled(qa, sa, qw, sw)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"q1x128 of A[:{rows}] + q128x128 of W + exact-partial FP64 GEMM {rows}x{N}x{K}; {dt:.2f} s",
+            "host_cpus_affinity": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,439 @@
+// Online tile quantizers: BF16 -> E4M3 codes + FP32 scales (gfx950).
+//
+// 1x128 tiles for activations and 128x128 blocks for weights [p1¶3, the
+// description of Figure 7(a)], the tile maximum taken online at quantization
+// time [p2¶4]; 128x1 tiles along tokens with transposed output for the Wgrad
+// operands [p5¶4].  Citations [pN¶k]: N-th page of the source collection, k-th
+// paragraph (p1 = xn--9g3bo1gtkw0l8ubf92bgle.kr wr_id 85187, p2 =
+// inprokorea.com wr_id 735329, p5 = inprokorea.com wr_id 890463).
+//
+// All three are single HBM passes: each BF16 element is read once, its code
+// written once, one FP32 scale written per tile.  The tile maximum is an
+// integer maximum over BF16 magnitude bits, reduced across lanes with DPP row
+// operations (1x128: one 128-element tile = 16 lanes x 16 bytes = one DPP row).
+#include "fp8_device.h"
+#include "host_common.h"
+
+namespace fp8blk {
+
+// Load up to 8 BF16 elements of a row chunk starting at p; `avail` elements
+// remain in the row.  Elements past the row end read as +0 (no effect on the
+// maximum) and are never stored.
+__device__ __forceinline__ uint4 load_chunk8(const uint16_t* p, int64_t avail) {
+  if (avail >= 8) return *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int j = 0; j < 8 && j < avail; ++j) w[j >> 1] |= (uint32_t)p[j] << ((j & 1) * 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ void store_chunk8(uint8_t* p, int64_t avail, uint2 c) {
+  if (avail >= 8) {
+    *reinterpret_cast<uint2*>(p) = c;
+    return;
+  }
+  for (int j = 0; j < 8 && j < avail; ++j) p[j] = (uint8_t)(((j < 4 ? c.x : c.y) >> ((j & 3) * 8)) & 0xFF);
+}
+
+__device__ __forceinline__ uint32_t chunk_abs_max(const uint4& v) {
+  uint32_t a = 0;
+  a = abs_max_bits(a, v.x);
+  a = abs_max_bits(a, v.y);
+  a = abs_max_bits(a, v.z);
+  a = abs_max_bits(a, v.w);
+  return a;
+}
+
+// ---------------------------------------------------------------------------
+// 1x128: a workgroup of 256 lanes covers 64 rows x one 128-column group.
+// Lane (sub = tid/16, c16 = tid%16) holds bytes [16*c16, 16*c16+16) of the
+// tile's 256 bytes for rows sub, sub+16, sub+32, sub+48.  Workgroups walk the
+// column groups of a 64-row band consecutively (g fastest) so that each band's
+// rows are read front to back.
+// ---------------------------------------------------------------------------
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                      int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                      float* __restrict__ s, int64_t G) {
+  const int64_t bid = blockIdx.x;
+  const int64_t g = bid % G;
+  const int64_t mb = bid / G;
+  const int sub = threadIdx.x >> 4;
+  const int c16 = threadIdx.x & 15;
+  const int64_t col = g * 128 + c16 * 8;
+  const int64_t avail = K - col;
+
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = mb * 64 + sub + 16 * i;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (row < M && avail > 0) v[i] = load_chunk8(x + row * ldx + col, avail);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = mb * 64 + sub + 16 * i;
+    const uint32_t amax = row16_max(chunk_abs_max(v[i]));  // all 16 lanes of the row active
+    const TileScale ts = make_scale<POW2, true>(amax << 16);
+    const uint2 codes = quantize8<POW2>(v[i], ts);
+    if (row < M) {
+      if (avail > 0) store_chunk8(q + row * ldq + col, avail, codes);
+      if (c16 == 0) s[g * M + row] = ts.s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 blocks: one workgroup per block, 64 elements per lane held in
+// registers between the block-wide maximum and the encode.
+// ---------------------------------------------------------------------------
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quant_block128(const uint16_t* __restrict__ w, int64_t R, int64_t C,
+                                                         int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
+                                                         float* __restrict__ s, int64_t GC) {
+  __shared__ uint32_t red[4];
+  const int64_t bj = blockIdx.x, bi = blockIdx.y;
+  const int sub = threadIdx.x >> 4;
+  const int c16 = threadIdx.x & 15;
+  const int64_t col = bj * 128 + c16 * 8;
+  const int64_t avail = C - col;
+
+  uint4 v[8];
+  uint32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = bi * 128 + sub + 16 * i;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (row < R && avail > 0) v[i] = load_chunk8(w + row * ldw + col, avail);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = max(a, chunk_abs_max(v[i]));
+  a = row16_max(a);
+  a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = max(max(red[0], red[1]), max(red[2], red[3]));
+  const TileScale ts = make_scale<POW2, true>(a << 16);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = bi * 128 + sub + 16 * i;
+    const uint2 codes = quantize8<POW2>(v[i], ts);
+    if (row < R && avail > 0) store_chunk8(q + row * ldq + col, avail, codes);
+  }
+  if (threadIdx.x == 0) s[bi * GC + bj] = ts.s;
+}
+
+// ---------------------------------------------------------------------------
+// 128x1 with transposed output: one workgroup per 128 tokens x 128 channels.
+// Lane (rb = tid/16, c16 = tid%16) loads tokens 8rb..8rb+7 of channels
+// 8*c16..8*c16+7.  Column maxima: per lane over its 8 tokens (packed 16-bit
+// max), across the 4 token groups of the wave by lane exchange, across the
+// 4 waves through LDS.  Codes go through an LDS tile laid out [channel][token]
+// so that the transposed rows of qT are written as contiguous 16-byte chunks.
+// The tile's 8-byte segments are XOR-swizzled by channel/8 to spread banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  const uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
+  const uint32_t hi = max(a >> 16, b >> 16);
+  return lo | (hi << 16);
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quant_128x1(const uint16_t* __restrict__ x, int64_t T, int64_t C,
+                                                      int64_t ldx, uint8_t* __restrict__ qT, int64_t ldqT,
+                                                      float* __restrict__ s) {
+  __shared__ uint32_t red[4][16][4];
+  __shared__ float sh_s[128], sh_r[128];
+  __shared__ int sh_slow[128];
+  __shared__ __align__(16) uint8_t tile[128 * 128];
+
+  const int64_t c0 = (int64_t)blockIdx.x * 128;
+  const int64_t t0 = (int64_t)blockIdx.y * 128;
+  const int tid = threadIdx.x;
+  const int c16 = tid & 15;
+  const int rb = tid >> 4;
+  const int64_t col = c0 + c16 * 8;
+  const int64_t avail = C - col;
+
+  uint4 v[8];
+  uint32_t m2[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t t = t0 + rb * 8 + j;
+    v[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (t < T && avail > 0) v[j] = load_chunk8(x + t * ldx + col, avail);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    m2[0] = pk_max_u16(m2[0], v[j].x & 0x7FFF7FFFu);
+    m2[1] = pk_max_u16(m2[1], v[j].y & 0x7FFF7FFFu);
+    m2[2] = pk_max_u16(m2[2], v[j].z & 0x7FFF7FFFu);
+    m2[3] = pk_max_u16(m2[3], v[j].w & 0x7FFF7FFFu);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m2[i] = pk_max_u16(m2[i], (uint32_t)__shfl_xor((int)m2[i], 16));
+    m2[i] = pk_max_u16(m2[i], (uint32_t)__shfl_xor((int)m2[i], 32));
+  }
+  if ((tid & 63) < 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[tid >> 6][c16][i] = m2[i];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int c = tid, cc = c >> 3, pair = (c & 7) >> 1, half = c & 1;
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t d = red[w][cc][pair];
+      a = max(a, half ? (d >> 16) : (d & 0xFFFFu));
+    }
+    const TileScale ts = make_scale<POW2, true>(a << 16);
+    sh_s[c] = ts.s;
+    sh_r[c] = ts.r;
+    sh_slow[c] = ts.slow ? 1 : 0;
+    if (c0 + c < C) s[(int64_t)blockIdx.y * C + c0 + c] = ts.s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c16 * 8 + i;
+    TileScale ts;
+    ts.s = sh_s[c];
+    ts.r = sh_r[c];
+    ts.slow = sh_slow[c] != 0;
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t wd = (i >> 1) == 0 ? v[j].x : (i >> 1) == 1 ? v[j].y : (i >> 1) == 2 ? v[j].z : v[j].w;
+      const float xv = (i & 1) ? bf16_hi(wd) : bf16_lo(wd);
+      y[j] = quotient_fast<POW2, true>(xv, ts);
+    }
+    if (__builtin_expect(ts.slow, 0)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t wd = (i >> 1) == 0 ? v[j].x : (i >> 1) == 1 ? v[j].y : (i >> 1) == 2 ? v[j].z : v[j].w;
+        y[j] = quotient_slow((i & 1) ? bf16_hi(wd) : bf16_lo(wd), ts.s);
+      }
+    }
+    uint2 codes;
+    codes.x = pack4_e4m3(y[0], y[1], y[2], y[3]);
+    codes.y = pack4_e4m3(y[4], y[5], y[6], y[7]);
+    const int seg = rb ^ c16;  // token segment rb of channel c, swizzled by c/8
+    *reinterpret_cast<uint2*>(tile + c * 128 + seg * 8) = codes;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int chunk = tid + 256 * k;
+    const int c = chunk >> 3;
+    const int part = chunk & 7;  // tokens 16*part .. 16*part+15
+    if (c0 + c >= C) continue;
+    const int sw = c >> 3;
+    const uint2 lo = *reinterpret_cast<const uint2*>(tile + c * 128 + ((2 * part) ^ sw) * 8);
+    const uint2 hi = *reinterpret_cast<const uint2*>(tile + c * 128 + ((2 * part + 1) ^ sw) * 8);
+    const int64_t t = t0 + 16 * part;
+    uint8_t* dst = qT + (c0 + c) * ldqT + t;
+    if (t + 16 <= T) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      const uint32_t wds[4] = {lo.x, lo.y, hi.x, hi.y};
+      for (int j = 0; j < 16 && t + j < T; ++j) dst[j] = (uint8_t)((wds[j >> 2] >> ((j & 3) * 8)) & 0xFF);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Re-quantization of a cached 1x128-quantized activation into transposed
+// 128x1 tiles [p5¶4]: codes are decoded by the hardware (exact), multiplied by
+// their 1x128 scale in FP32 (one rounding), and the resulting FP32 values are
+// quantized along tokens exactly as k_quant_128x1 quantizes BF16 values.  The
+// dequantized values are general FP32 numbers, outside the domain the
+// division shortcut was checked on, so the default mode divides per element
+// (IEEE); power-of-two scales multiply by the exact reciprocal.
+// One workgroup per 128 tokens x 128 channels; the 128-channel block is also
+// exactly one 1x128 scale group, so each token has one input scale here.
+// ---------------------------------------------------------------------------
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 load_codes8(const uint8_t* p, int64_t avail) {
+  if (avail >= 8) return *reinterpret_cast<const uint2*>(p);
+  uint32_t w[2] = {0u, 0u};
+  for (int j = 0; j < 8 && j < avail; ++j) w[j >> 2] |= (uint32_t)p[j] << ((j & 3) * 8);
+  return make_uint2(w[0], w[1]);
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_requant_128x1(const uint8_t* __restrict__ q, const float* __restrict__ sq,
+                                                        int64_t T, int64_t C, int64_t ldq, uint8_t* __restrict__ qT,
+                                                        int64_t ldqT, float* __restrict__ sT) {
+  __shared__ uint32_t red[4][16][8];
+  __shared__ float sh_s[128], sh_r[128];
+  __shared__ int sh_slow[128];
+  __shared__ __align__(16) uint8_t tile[128 * 128];
+
+  const int64_t c0 = (int64_t)blockIdx.x * 128;
+  const int64_t t0 = (int64_t)blockIdx.y * 128;
+  const int tid = threadIdx.x;
+  const int c16 = tid & 15;
+  const int rb = tid >> 4;
+  const int64_t col = c0 + c16 * 8;
+  const int64_t avail = C - col;
+
+  float xv[8][8];  // [token j][channel i]
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t t = t0 + rb * 8 + j;
+    uint2 v = make_uint2(0u, 0u);
+    float so = 0.0f;
+    if (t < T) {
+      if (avail > 0) v = load_codes8(q + t * ldq + col, avail);
+      so = sq[(int64_t)blockIdx.x * T + t];
+    }
+    const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
+    const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+    const v2f d45 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
+    const v2f d67 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+    xv[j][0] = d01[0] * so; xv[j][1] = d01[1] * so;
+    xv[j][2] = d23[0] * so; xv[j][3] = d23[1] * so;
+    xv[j][4] = d45[0] * so; xv[j][5] = d45[1] * so;
+    xv[j][6] = d67[0] * so; xv[j][7] = d67[1] * so;
+  }
+  uint32_t m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = max(a, __float_as_uint(xv[j][i]) & 0x7FFFFFFFu);
+    a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+    m[i] = a;
+  }
+  if ((tid & 63) < 16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[tid >> 6][c16][i] = m[i];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int c = tid;
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) a = max(a, red[w][c >> 3][c & 7]);
+    const TileScale ts = make_scale<POW2, false>(a);
+    sh_s[c] = ts.s;
+    sh_r[c] = ts.r;
+    sh_slow[c] = ts.slow ? 1 : 0;
+    if (c0 + c < C) sT[(int64_t)blockIdx.y * C + c0 + c] = ts.s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c16 * 8 + i;
+    TileScale ts;
+    ts.s = sh_s[c];
+    ts.r = sh_r[c];
+    ts.slow = sh_slow[c] != 0;
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = quotient_fast<POW2, false>(xv[j][i], ts);
+    if (POW2 && __builtin_expect(ts.slow, 0)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = quotient_slow(xv[j][i], ts.s);
+    }
+    uint2 codes;
+    codes.x = pack4_e4m3(y[0], y[1], y[2], y[3]);
+    codes.y = pack4_e4m3(y[4], y[5], y[6], y[7]);
+    *reinterpret_cast<uint2*>(tile + c * 128 + ((rb ^ c16) * 8)) = codes;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int chunk = tid + 256 * k;
+    const int c = chunk >> 3;
+    const int part = chunk & 7;
+    if (c0 + c >= C) continue;
+    const int sw = c >> 3;
+    const uint2 lo = *reinterpret_cast<const uint2*>(tile + c * 128 + ((2 * part) ^ sw) * 8);
+    const uint2 hi = *reinterpret_cast<const uint2*>(tile + c * 128 + ((2 * part + 1) ^ sw) * 8);
+    const int64_t t = t0 + 16 * part;
+    uint8_t* dst = qT + (c0 + c) * ldqT + t;
+    if (t + 16 <= T) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      const uint32_t wds[4] = {lo.x, lo.y, hi.x, hi.y};
+      for (int j = 0; j < 16 && t + j < T; ++j) dst[j] = (uint8_t)((wds[j >> 2] >> ((j & 3) * 8)) & 0xFF);
+    }
+  }
+}
+
+}  // namespace fp8blk
+
+using namespace fp8blk;
+
+extern "C" fp8blk_status_t fp8blk_quantize_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                                 int64_t ldq, float* s, uint32_t flags, void* stream) {
+  if (flags & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(x, M, K, ldx, 2) || !matrix_ok(q, M, K, ldq, 1)) return FP8BLK_ERR_INVALID_ARG;
+  const int64_t G = ceil_div(K, 128);
+  if (!vec_ok(s, G * M)) return FP8BLK_ERR_INVALID_ARG;
+  if (M == 0 || K == 0) return FP8BLK_OK;
+  const int64_t blocks = ceil_div(M, 64) * G;
+  if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
+  if (flags & FP8BLK_SCALE_POW2)
+    hipLaunchKernelGGL(k_quant_1x128<true>, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream), x, M, K, ldx, q,
+                       ldq, s, G);
+  else
+    hipLaunchKernelGGL(k_quant_1x128<false>, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream), x, M, K, ldx,
+                       q, ldq, s, G);
+  return launch_status();
+}
+
+extern "C" fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
+                                                    uint8_t* q, int64_t ldq, float* s, uint32_t flags,
+                                                    void* stream) {
+  if (flags & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(w, R, C, ldw, 2) || !matrix_ok(q, R, C, ldq, 1)) return FP8BLK_ERR_INVALID_ARG;
+  const int64_t GR = ceil_div(R, 128), GC = ceil_div(C, 128);
+  if (!vec_ok(s, GR * GC)) return FP8BLK_ERR_INVALID_ARG;
+  if (R == 0 || C == 0) return FP8BLK_OK;
+  if (GC > 0x7FFFFFFF || GR > 65535) return FP8BLK_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)GC, (unsigned)GR);
+  if (flags & FP8BLK_SCALE_POW2)
+    hipLaunchKernelGGL(k_quant_block128<true>, grid, dim3(256), 0, as_stream(stream), w, R, C, ldw, q, ldq, s, GC);
+  else
+    hipLaunchKernelGGL(k_quant_block128<false>, grid, dim3(256), 0, as_stream(stream), w, R, C, ldw, q, ldq, s, GC);
+  return launch_status();
+}
+
+extern "C" fp8blk_status_t fp8blk_quantize_128x1(const uint16_t* x, int64_t T, int64_t C, int64_t ldx, uint8_t* qT,
+                                                 int64_t ldqT, float* s, uint32_t flags, void* stream) {
+  if (flags & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(x, T, C, ldx, 2) || !matrix_ok(qT, C, T, ldqT, 1)) return FP8BLK_ERR_INVALID_ARG;
+  const int64_t GT = ceil_div(T, 128), GC = ceil_div(C, 128);
+  if (!vec_ok(s, GT * C)) return FP8BLK_ERR_INVALID_ARG;
+  if (T == 0 || C == 0) return FP8BLK_OK;
+  if (GC > 0x7FFFFFFF || GT > 65535) return FP8BLK_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)GC, (unsigned)GT);
+  if (flags & FP8BLK_SCALE_POW2)
+    hipLaunchKernelGGL(k_quant_128x1<true>, grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT, s);
+  else
+    hipLaunchKernelGGL(k_quant_128x1<false>, grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT, s);
+  return launch_status();
+}
+
+extern "C" fp8blk_status_t fp8blk_requantize_128x1_from_1x128(const uint8_t* q, const float* sq, int64_t T, int64_t C,
+                                                              int64_t ldq, uint8_t* qT, int64_t ldqT, float* sT,
+                                                              uint32_t flags, void* stream) {
+  if (flags & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(q, T, C, ldq, 1) || !matrix_ok(qT, C, T, ldqT, 1)) return FP8BLK_ERR_INVALID_ARG;
+  const int64_t GT = ceil_div(T, 128), GC = ceil_div(C, 128);
+  if (!vec_ok(sq, GC * T) || !vec_ok(sT, GT * C)) return FP8BLK_ERR_INVALID_ARG;
+  if (T == 0 || C == 0) return FP8BLK_OK;
+  if (GC > 0x7FFFFFFF || GT > 65535) return FP8BLK_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)GC, (unsigned)GT);
+  if (flags & FP8BLK_SCALE_POW2)
+    hipLaunchKernelGGL(k_requant_128x1<true>, grid, dim3(256), 0, as_stream(stream), q, sq, T, C, ldq, qT, ldqT, sT);
+  else
+    hipLaunchKernelGGL(k_requant_128x1<false>, grid, dim3(256), 0, as_stream(stream), q, sq, T, C, ldq, qT, ldqT, sT);
+  return launch_status();
+}

@@ -1,0 +1,203 @@
+/*
+ * libfp8blk — fine-grained (tile/block-scaled) FP8 quantization and FP8 GEMM
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method: activations are quantized to E4M3 with one FP32 scale per 1x128
+ * tile (one token, 128 channels) and weights with one scale per 128x128 block
+ * [p1¶3, the description of Figure 7(a)]; the tile maximum is taken online at
+ * quantization time [p2¶4]; E4M3 is used for every tensor [p2¶2]; power-of-two
+ * scales are used for some activations [p2¶4]; the GEMM multiplies the FP8
+ * codes and promotes each 128-deep K group's partial sum into an FP32
+ * accumulator, multiplying in the group's scales there [p2¶3, p2¶4]; Fprop,
+ * Dgrad and Wgrad all run in FP8 [p1¶3, Figure 6], Wgrad on operands
+ * re-quantized into 128x1 tiles along tokens [p5¶4]; MoE expert projections
+ * use a per-expert (grouped) variant [p2¶4].
+ *
+ * Citations [pN¶k] name the N-th page of the source collection and its k-th
+ * paragraph counted from the page heading:
+ *   p1 = xn--9g3bo1gtkw0l8ubf92bgle.kr (board qna, wr_id 85187)
+ *   p2 = inprokorea.com (board free, wr_id 735329)
+ *   p5 = inprokorea.com (board free, wr_id 890463)
+ *
+ * Numerics fixed by this library where the pages are silent:
+ *   E4M3 is OCP "e4m3fn" (bias 7, no infinities, largest finite 448).
+ *   scale s = fl32(amax / 448) (IEEE division); with FP8BLK_SCALE_POW2,
+ *   s = the smallest power of two >= amax / 448 (exact); amax = 0 gives s = 1.
+ *   code q = E4M3(fl32(x / s)), round to nearest even, saturating to +-448,
+ *   sign kept for values that round to zero.  Dequantized value: dec(q) * s.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) on
+ *     the current HIP device.  The caller owns every buffer; the library never
+ *     allocates, frees or synchronizes, and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued asynchronously on it.
+ *   - BF16 inputs are raw bit patterns (uint16_t).  Matrices are row-major
+ *     with leading dimension (row pitch) in ELEMENTS.
+ *   - Inputs and outputs must not overlap.
+ *   - Sizes of zero are valid and enqueue nothing.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns FP8BLK_ERR_INVALID_ARG and touches nothing.
+ *     FP8BLK_ERR_LAUNCH reports a failed kernel launch.  Faults inside a
+ *     kernel surface at the caller's next synchronization (HIP convention).
+ *   - Alignment: every matrix pointer must be 16-byte aligned and every row
+ *     pitch a multiple of 16 bytes (8 BF16, 16 FP8 codes, 4 FP32); scale
+ *     pointers must be 4-byte aligned.
+ *   - Extent: a matrix with R rows and pitch P occupies R*P elements; the
+ *     GEMMs may read (never write) the padding between the row length and
+ *     the pitch, including that of the last row.
+ */
+#ifndef LIBFP8BLK_H
+#define LIBFP8BLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BLK_OK = 0,
+  FP8BLK_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad pitch/alignment, unknown flag/enum */
+  FP8BLK_ERR_UNSUPPORTED = 2, /* valid but not implemented combination */
+  FP8BLK_ERR_LAUNCH = 3       /* hipGetLastError() reported a failure after a launch */
+} fp8blk_status_t;
+
+/* flags for the quantizers */
+#define FP8BLK_SCALE_POW2 0x1u /* power-of-two scales [p2¶4] */
+
+/* storage of the GEMM's B operand */
+enum { FP8BLK_OP_N = 0, /* B stored [K][N] (row pitch ldb >= N)            */
+       FP8BLK_OP_T = 1  /* B stored [N][K] (row pitch ldb >= K)            */ };
+
+/* B scale layouts */
+enum { FP8BLK_BSCALE_BLOCK128 = 0, /* one scale per 128x128 block of B as stored:
+                                      [K/128][ceil(N/128)] for OP_N,
+                                      [ceil(N/128)][K/128] for OP_T          */
+       FP8BLK_BSCALE_ROW128 = 1    /* one scale per column n per K group:
+                                      [K/128][N] (B quantized with 128-deep
+                                      tiles along K, e.g. by quantize_128x1) */ };
+
+/*
+ * 1x128 quantization of activations (per token per 128 channels) [p1¶3],
+ * amax taken online per tile [p2¶4].
+ *   x   [M][K] BF16, pitch ldx >= K.
+ *   q   [M][K] E4M3 codes (uint8), pitch ldq >= K.
+ *   s   [ceil(K/128)][M] FP32, dense: s[g*M + m] scales row m, columns
+ *       [128g, 128g+128); a partial last group uses the columns present.
+ *   flags: 0 or FP8BLK_SCALE_POW2.
+ */
+fp8blk_status_t fp8blk_quantize_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* s, uint32_t flags,
+                                      void* stream);
+
+/*
+ * 128x1 quantization along tokens with transposed output, the Wgrad operand
+ * layout [p5¶4].
+ *   x   [T][C] BF16 (tokens x channels), pitch ldx >= C.
+ *   qT  [C][T] E4M3 codes, pitch ldqT >= T: qT[c*ldqT + t] is token t, channel c.
+ *   s   [ceil(T/128)][C] FP32, dense: s[g*C + c] scales channel c over tokens
+ *       [128g, 128g+128).  qT/s equal quantize_1x128 applied to x transposed.
+ *   flags: 0 or FP8BLK_SCALE_POW2.
+ */
+fp8blk_status_t fp8blk_quantize_128x1(const uint16_t* x, int64_t T, int64_t C, int64_t ldx,
+                                      uint8_t* qT, int64_t ldqT, float* s, uint32_t flags,
+                                      void* stream);
+
+/*
+ * 128x128 block quantization of weights (per 128 input channels per 128
+ * output channels) [p1¶3].
+ *   w   [R][C] BF16, pitch ldw >= C.
+ *   q   [R][C] E4M3 codes, pitch ldq >= C.
+ *   s   [ceil(R/128)][ceil(C/128)] FP32, dense; partial edge blocks use the
+ *       elements present.
+ *   flags: 0 or FP8BLK_SCALE_POW2.
+ */
+fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
+                                         uint8_t* q, int64_t ldq, float* s, uint32_t flags,
+                                         void* stream);
+
+/*
+ * Re-quantization of a cached 1x128-quantized activation into transposed
+ * 128x1 tiles: read, dequantize, transpose, re-quantize, store [p5¶4].
+ *   q   [T][C] E4M3 codes from fp8blk_quantize_1x128 (pitch ldq >= C),
+ *   sq  [ceil(C/128)][T] its FP32 scales.
+ *   The dequantized value is fl32(dec(q) * s); it is then quantized exactly
+ *   as fp8blk_quantize_128x1 quantizes a value.
+ *   qT  [C][T] E4M3 codes (pitch ldqT >= T), sT [ceil(T/128)][C] FP32.
+ */
+fp8blk_status_t fp8blk_requantize_128x1_from_1x128(const uint8_t* q, const float* sq, int64_t T,
+                                                   int64_t C, int64_t ldq, uint8_t* qT,
+                                                   int64_t ldqT, float* sT, uint32_t flags,
+                                                   void* stream);
+
+/*
+ * Block-scaled FP8 GEMM:  C[m][n] = sum_g sA[g][m] * sB(g,n) * P_g[m][n],
+ *   P_g[m][n] = sum over the 128-deep K group g of dec(A[m][k]) * dec(B[k][n]).
+ * Each group's partial is formed by the matrix cores (one MFMA per 16x16
+ * output tile and group) and promoted into an FP32 accumulator with one FMA
+ * by the scale product [p2¶3, p2¶4].
+ *   A  [M][K] E4M3 codes, pitch lda >= K; sA [K/128][M] FP32 (1x128 scales).
+ *   B  [K][N] (opB = FP8BLK_OP_N, pitch ldb >= N) or [N][K] (FP8BLK_OP_T,
+ *      pitch ldb >= K) E4M3 codes; sB per `bscale_mode`.
+ *   C  [M][N] FP32, pitch ldc >= N (overwritten).
+ *   K must be a positive multiple of 128 (M, N arbitrary).
+ *   Roles: Fprop Y = X W (A = 1x128-quantized X, B = W [K][N] block-scaled,
+ *   OP_N); Dgrad dX = dY W^T (A = 1x128-quantized dY, B = the same W read as
+ *   OP_T with its own block scales); Wgrad dW = X^T dY (A = 128x1-quantized
+ *   X as [d_in][T], B = 128x1-quantized dY as [d_out][T] with OP_T and
+ *   FP8BLK_BSCALE_ROW128) [p1¶3; p5¶4].
+ *   workspace / workspace_bytes: reserved for split-K partials; pass NULL/0
+ *   (fp8blk_workspace_bytes returns 0 for every shape in this version).
+ */
+fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
+                                            const uint8_t* A, int64_t lda, const float* sA,
+                                            const uint8_t* B, int64_t ldb, int opB,
+                                            const float* sB, int bscale_mode,
+                                            float* C, int64_t ldc,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/*
+ * Grouped (per-expert) block-scaled FP8 GEMM for MoE expert projections
+ * [p2¶4]: for each expert e,
+ *   C[off[e]:off[e+1]][:] = A[off[e]:off[e+1]][:] * B_e
+ * with the same arithmetic as fp8blk_gemm_fp8_blockscaled.
+ *   group_offsets  DEVICE int32 [G+1], non-decreasing, off[0] = 0,
+ *                  off[G] = M_total (rows of A/C ordered by expert; groups
+ *                  may be empty).  Read on the device: no host sync.
+ *   A   [M_total][K] codes, pitch lda; sA [K/128][M_total].
+ *   B   G matrices, expert e at B + e*strideB (elements), each [K][N]
+ *       (OP_N, pitch ldb >= N) or [N][K] (OP_T, pitch ldb >= K).
+ *   sB  G block-scale tables (BLOCK128 layout of one B_e), expert e at
+ *       sB + e*stride_sB (floats).
+ *   C   [M_total][N] FP32, pitch ldc.
+ *   max_group_rows: an upper bound on any group's row count (e.g. M_total);
+ *   it only sizes the launch grid.
+ *   K must be a positive multiple of 128.
+ */
+fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(int64_t G, const int32_t* group_offsets,
+                                                    int64_t M_total, int64_t max_group_rows,
+                                                    int64_t N, int64_t K,
+                                                    const uint8_t* A, int64_t lda, const float* sA,
+                                                    const uint8_t* B, int64_t ldb, int64_t strideB,
+                                                    int opB, const float* sB, int64_t stride_sB,
+                                                    float* C, int64_t ldc,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    void* stream);
+
+/* Scratch bytes the GEMMs need for the given shape (0: none needed). */
+size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
+
+/* Human-readable name of a status code (static string). */
+const char* fp8blk_status_string(fp8blk_status_t status);
+
+/* ABI version of this header: 1. */
+int fp8blk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFP8BLK_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every symbol the public header declares,
+and rejects invalid arguments on the host before anything is enqueued.
+
+CPU only: every call here either fails validation or has an empty shape, so
+no HIP runtime call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_fine_grained_quantize_amd as fb
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "libfp8blk.h")
+
+INVALID, OK = 1, 0
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8blk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_is_built():
+    assert os.path.exists(fb.library_path), "run python -m fp8_fine_grained_quantize_amd.build"
+
+
+def test_exports_every_declared_symbol():
+    L = fb.lib()
+    declared = _declared()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(fb.EXPORTED_SYMBOLS) == declared
+
+
+def test_version_and_status_strings():
+    assert fb.abi_version() == 1
+    assert fb.status_string(0) == "FP8BLK_OK"
+    assert fb.status_string(1) == "FP8BLK_ERR_INVALID_ARG"
+    assert fb.status_string(2) == "FP8BLK_ERR_UNSUPPORTED"
+    assert fb.status_string(3) == "FP8BLK_ERR_LAUNCH"
+    assert fb.workspace_bytes(4096, 4096, 7168, 1) == 0
+
+
+P = ctypes.c_void_p
+FAKE = P(0x100000)     # never dereferenced: every call below fails validation
+MIS = P(0x100004)      # misaligned for 16-byte matrices
+NULL = P(0)
+
+
+@pytest.mark.parametrize("fn", ["fp8blk_quantize_1x128", "fp8blk_quantize_128x1", "fp8blk_quantize_block128"])
+def test_quantizer_validation(fn):
+    f = getattr(fb.lib(), fn)
+    # null input
+    assert f(NULL, 4, 128, 128, FAKE, 128, FAKE, 0, NULL) == INVALID
+    # null output / scales
+    assert f(FAKE, 4, 128, 128, NULL, 128, FAKE, 0, NULL) == INVALID
+    assert f(FAKE, 4, 128, 128, FAKE, 128, NULL, 0, NULL) == INVALID
+    # negative sizes
+    assert f(FAKE, -1, 128, 128, FAKE, 128, FAKE, 0, NULL) == INVALID
+    assert f(FAKE, 4, -128, 128, FAKE, 128, FAKE, 0, NULL) == INVALID
+    # unknown flag
+    assert f(FAKE, 4, 128, 128, FAKE, 128, FAKE, 0x2, NULL) == INVALID
+    # pitch below the row length, or not a multiple of 16 bytes
+    if fn == "fp8blk_quantize_128x1":
+        assert f(FAKE, 4, 128, 120, FAKE, 16, FAKE, 0, NULL) == INVALID  # ldx < C
+        assert f(FAKE, 4, 128, 128, FAKE, 4, FAKE, 0, NULL) == INVALID   # ldqT not 16-byte multiple
+        assert f(FAKE, 40, 128, 128, FAKE, 32, FAKE, 0, NULL) == INVALID  # ldqT < T
+    else:
+        assert f(FAKE, 4, 128, 120, FAKE, 128, FAKE, 0, NULL) == INVALID
+        assert f(FAKE, 4, 128, 132, FAKE, 132, FAKE, 0, NULL) == INVALID
+        assert f(FAKE, 4, 128, 128, FAKE, 112, FAKE, 0, NULL) == INVALID
+    # misaligned matrix pointer
+    assert f(MIS, 4, 128, 128, FAKE, 128, FAKE, 0, NULL) == INVALID
+    # empty shapes are valid no-ops (nothing enqueued)
+    assert f(NULL, 0, 128, 128, NULL, 128, NULL, 0, NULL) == OK
+    assert f(NULL, 4, 0, 128, NULL, 128, NULL, 0, NULL) == OK
+
+
+def test_requantize_validation():
+    f = fb.lib().fp8blk_requantize_128x1_from_1x128
+    assert f(NULL, FAKE, 256, 128, 128, FAKE, 256, FAKE, 0, NULL) == INVALID
+    assert f(FAKE, NULL, 256, 128, 128, FAKE, 256, FAKE, 0, NULL) == INVALID
+    assert f(FAKE, FAKE, 256, 128, 128, FAKE, 256, FAKE, 4, NULL) == INVALID
+    assert f(FAKE, FAKE, 256, 128, 100, FAKE, 256, FAKE, 0, NULL) == INVALID
+    assert f(NULL, NULL, 0, 128, 128, NULL, 16, NULL, 0, NULL) == OK
+
+
+def _gemm(M=256, N=256, K=256, A=FAKE, lda=256, sA=FAKE, B=FAKE, ldb=256, opB=0, sB=FAKE, mode=0, C=FAKE,
+          ldc=256):
+    return fb.lib().fp8blk_gemm_fp8_blockscaled(M, N, K, A, lda, sA, B, ldb, opB, sB, mode, C, ldc, NULL, 0, NULL)
+
+
+def test_gemm_validation():
+    assert _gemm(K=200) == INVALID            # K % 128
+    assert _gemm(K=0) == INVALID
+    assert _gemm(M=-1) == INVALID
+    assert _gemm(opB=2) == INVALID
+    assert _gemm(mode=5) == INVALID
+    assert _gemm(A=NULL) == INVALID
+    assert _gemm(B=NULL) == INVALID
+    assert _gemm(C=NULL) == INVALID
+    assert _gemm(sA=NULL) == INVALID
+    assert _gemm(sB=NULL) == INVALID
+    assert _gemm(lda=128) == INVALID           # lda < K
+    assert _gemm(ldb=100) == INVALID           # not a 16-byte multiple
+    assert _gemm(ldc=255) == INVALID           # < N
+    assert _gemm(opB=1, ldb=128) == INVALID    # [N][K] needs ldb >= K
+    assert _gemm(A=MIS) == INVALID
+    assert _gemm(M=0) == OK and _gemm(N=0) == OK
+
+
+def test_grouped_validation():
+    f = fb.lib().fp8blk_grouped_gemm_fp8_blockscaled
+
+    def call(G=4, off=FAKE, Mt=256, mgr=0, N=256, K=256, A=FAKE, lda=256, sA=FAKE, B=FAKE, ldb=256,
+             strideB=65536, opB=0, sB=FAKE, ssB=4, C=FAKE, ldc=256):
+        return f(G, off, Mt, mgr, N, K, A, lda, sA, B, ldb, strideB, opB, sB, ssB, C, ldc, NULL, 0, NULL)
+
+    assert call(off=NULL) == INVALID
+    assert call(K=100) == INVALID
+    assert call(strideB=1000) == INVALID       # below one expert's matrix
+    assert call(ssB=1) == INVALID              # below one expert's scale table
+    assert call(opB=3) == INVALID
+    assert call(G=-1) == INVALID
+    assert call(G=0) == OK and call(Mt=0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fb, "library_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fb, "_LIB", None)
+    with pytest.raises(fb.Fp8BlkError):
+        fb.lib()
