@@ -43,7 +43,21 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB (src) -> 1 GiB (dst) a few times; "
+                         "its FETCH_SIZE/WRITE_SIZE counters scale the quantizers' and GEMM's")
     return ap.parse_args()
+
+
+def calibrate_copy(torch):
+    """A plain copy kernel of known size: 2^30 bytes read, 2^30 written per launch."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t = timed_events(torch, lambda i: dst.copy_(src), 5)
+    gbs = 2 * (1 << 30) / (t * 1e-3) / 1e9
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 1 << 30,
+                      "bytes_written_per_launch": 1 << 30, "us": round(t * 1e3, 2), "GB/s": round(gbs, 1)}))
 
 
 def timed_events(torch, fn, reps):
@@ -67,6 +81,10 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
 
     import fp8_fine_grained_quantize_amd as fb
     import synthetic

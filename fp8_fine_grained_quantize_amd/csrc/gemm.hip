@@ -40,25 +40,51 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int WAVES_M_, int WAVES_N_, int TM_, int TN_>
+// Workgroup tile: WAVES_M x WAVES_N waves, each owning TM x TN MFMA tiles of
+// 16x16; STAGES LDS buffers in the copy pipeline (group g+STAGES-1 is in
+// flight while group g is computed).
+template <int WAVES_M_, int WAVES_N_, int TM_, int TN_, int STAGES_>
 struct TileCfg {
-  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, TM = TM_, TN = TN_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, TM = TM_, TN = TN_, STAGES = STAGES_;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int WTM = 16 * TM, WTN = 16 * TN;
   static constexpr int BM = WAVES_M * WTM, BN = WAVES_N * WTN;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int A_CHUNKS = A_BYTES / 16, B_CHUNKS = B_BYTES / 16;
+  static constexpr int A_ITERS = A_CHUNKS / (64 * NW), B_ITERS = B_CHUNKS / (64 * NW);
+  // Scale copies: BM floats of sA then BN floats of sB, 64 floats per wave
+  // instruction, spread so that every wave issues the same number of copies.
+  static constexpr int S_BLOCKS = (BM + BN) / 64;
+  static constexpr int S_ITERS = (S_BLOCKS + NW - 1) / NW;
+  static constexpr int LOADS_PER_STAGE = A_ITERS + B_ITERS + S_ITERS;  // per wave
   static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * BUF_BYTES + 2 * BM * 4 + 2 * BN * 4;
+  static constexpr int LDS_BYTES = STAGES * (BUF_BYTES + BM * 4 + BN * 4);
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must lie in one 128-column scale block");
   static_assert(BN >= 128, "the N-major swizzle needs BN >= 128");
   static_assert(A_CHUNKS % (64 * NW) == 0 && B_CHUNKS % (64 * NW) == 0, "whole 1 KB copy blocks per wave");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies in 64-float blocks");
+  static_assert(STAGES >= 2, "at least double buffering");
+  static_assert((STAGES - 2) * LOADS_PER_STAGE <= 63, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
-using SmallCfg = TileCfg<2, 2, 4, 4>;  // 128 x 128 tile, 4 waves of 64 x 64
-using BigCfg = TileCfg<2, 4, 8, 4>;    // 256 x 256 tile, 8 waves of 128 x 64
+#ifndef FP8BLK_BIG_CFG
+#define FP8BLK_BIG_CFG 2, 4, 8, 4, 2  // 256 x 256 tile, 8 waves of 128 x 64, double buffered
+#endif
+#ifndef FP8BLK_SMALL_CFG
+#define FP8BLK_SMALL_CFG 2, 2, 4, 4, 2  // 128 x 128 tile, 4 waves of 64 x 64
+#endif
+using BigCfg = TileCfg<FP8BLK_BIG_CFG>;
+using SmallCfg = TileCfg<FP8BLK_SMALL_CFG>;
+
+// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 // --- LDS addressing -------------------------------------------------------
 // K-major tile [rows][128 bytes]: 16-byte chunk c of row r lives at chunk
@@ -72,14 +98,30 @@ __device__ __forceinline__ int nmaj_off(int k, int m16) {
   return k * BN + ((m16 ^ (k & 7)) << 4);
 }
 
-// Direct global->LDS copies.  The LDS destination of lane i is base + size*i
-// (base uniform across the wave), so tile swizzles are applied by choosing,
-// for each lane, the global chunk that belongs at that LDS position.
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+// Direct global->LDS copies through buffer resources: buffer_load_dwordx4
+// (or _dword) with the lds modifier writes lane i's data at M0 + size*i, M0
+// uniform across the wave.  Tile swizzles are applied by choosing, for each
+// lane, the global chunk that belongs at its LDS position.  One per-lane
+// offset per operand is computed once per tile; successive copies of a group
+// differ by a scalar offset, and each K group only moves the scalar resource
+// base, so copies cost no vector arithmetic inside the K loop.
+//
+// Each resource's record count ends at the last valid byte of the operand
+// slab it covers: chunks of rows (or, for [K][N] B, of the final row) beyond
+// the matrix edge are out of range and read as zero.  Such rows and columns
+// only feed output rows/columns that are never stored (column n of C depends
+// only on column n of B, row m only on row m of A), as do the padding
+// columns of a [K][N] B tile that runs past N.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
+  // raw buffer (stride 0); 0x00020000 = gfx9 raw-buffer descriptor word 3
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 4, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int32_t soff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voff, 0, 0, 0);
 }
 
 // Arguments of one output tile: where its operands start and how far they
@@ -100,111 +142,149 @@ struct TileArgs {
   int64_t K;
 };
 
-// Copy K group g of the tile's operands and scales into one LDS buffer.
-// Operand rows or columns past the matrix edge are fetched from a clamped,
-// valid address: they only feed output rows/columns that are never stored
-// (column n of C depends only on column n of B, row m only on row m of A).
+// Copies of one K group.  Group bases: A tile A + k0; B tile B + n0*ldb + k0
+// ([N][K]) or B + k0*ldb + n0 ([K][N]); scales sA + g*ld and sB + g*ld + n0.
+// The sA copy is permuted so that each lane later reads the TM row scales it
+// needs (rows 16*i + lane%16 of its wave's rows) as one contiguous run.
 template <class CFG, bool OPB_T, bool ROW128>
-__device__ __forceinline__ void issue_tile_loads(const TileArgs& t, int g, uint8_t* buf, float* sAs_buf,
-                                                 float* sBs_buf) {
-  constexpr int BM = CFG::BM, BN = CFG::BN, NW = CFG::NW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t k0 = (int64_t)g * 128;
-  uint8_t* As = buf;
-  uint8_t* Bs = buf + CFG::A_BYTES;
-#pragma unroll
-  for (int it = 0; it < CFG::A_CHUNKS / (64 * NW); ++it) {
-    const int blk = it * NW + wave;  // 1 KB block of the A tile
-    const int ci = blk * 64 + lane;  // physical 16-byte chunk
-    const int r = ci >> 3, pc = ci & 7;
-    const int c = pc ^ ((r >> 1) & 7);
-    const int64_t rr = r < t.rows ? r : t.rows - 1;
-    dma16(t.A + rr * t.lda + k0 + c * 16, As + blk * 1024);
-  }
-#pragma unroll
-  for (int it = 0; it < CFG::B_CHUNKS / (64 * NW); ++it) {
-    const int blk = it * NW + wave;
-    const int ci = blk * 64 + lane;
-    if (OPB_T) {
-      const int r = ci >> 3, pc = ci & 7;
-      const int c = pc ^ ((r >> 1) & 7);
-      const int64_t n = t.n0 + r < t.N ? t.n0 + r : t.N - 1;
-      dma16(t.B + n * t.ldb + k0 + c * 16, Bs + blk * 1024);
+struct CopyPlan {
+  static constexpr int NW = CFG::NW, BM = CFG::BM, BN = CFG::BN;
+  static_assert(CFG::S_ITERS == 1, "one scale copy per wave");
+  // [K][N] B tile: BN/16 chunks per k row, so one copy iteration advances k
+  // by KSTEP rows; the row swizzle (k & 7) must repeat across iterations.
+  static constexpr int KSTEP = NW * 64 / (BN / 16);
+  static_assert(KSTEP % 8 == 0, "[K][N] copies keep the row swizzle across iterations");
+  uint32_t a, b, sc;
+  bool sc_is_b;  // uniform per wave
+
+  __device__ __forceinline__ void init(const TileArgs& t) {
+    constexpr int TM = CFG::TM, WTM = CFG::WTM;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    {  // A and [N][K] B: chunk ci = (it*NW + wave)*64 + lane; row ci/8 advances by 8*NW per it
+      const int ci = wave * 64 + lane;
+      const int r = ci >> 3, c = (ci & 7) ^ ((r >> 1) & 7);
+      a = (uint32_t)(r * t.lda + c * 16);
+      if (OPB_T) b = (uint32_t)(r * t.ldb + c * 16);
+    }
+    if (!OPB_T) {  // [K][N] B: BN/16 chunks per k row; k advances by KSTEP per it
+      constexpr int CPR = BN / 16;
+      const int ci = wave * 64 + lane;
+      const int k = ci / CPR, m = (ci % CPR) ^ (k & 7);
+      b = (uint32_t)(k * t.ldb + m * 16);
+    }
+    int blk = wave;
+    if (blk >= CFG::S_BLOCKS) blk = 0;  // surplus copy: rewrites block 0 with the same data
+    const int p = blk * 64 + lane;      // float position in the [BM + BN] scale buffer
+    if (p < BM) {
+      const int w = p / WTM, q = p % WTM;
+      sc = (uint32_t)((w * WTM + 16 * (q % TM) + q / TM) * 4);
+      sc_is_b = false;
     } else {
-      constexpr int CPR = BN / 16;  // chunks per k row
-      const int k = ci / CPR, pm = ci % CPR;
-      const int m = pm ^ (k & 7);
-      const int64_t col = t.n0 + m * 16;
-      dma16(t.B + (k0 + k) * t.ldb + (col < t.N ? col : 0), Bs + blk * 1024);
+      sc = ROW128 ? (uint32_t)((p - BM) * 4) : 0u;  // block-scale mode: the half is unused
+      sc_is_b = ROW128;
     }
   }
-  // scales: BM floats of sA (and BN of sB for ROW128), 64 per instruction
-  if (wave == 0) {
+
+  __device__ __forceinline__ void issue(const TileArgs& t, int g, uint8_t* buf, float* sbuf) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t k0 = (int64_t)g * 128;
+    const __amdgpu_buffer_rsrc_t ra = rsrc_of(t.A + k0, (t.rows - 1) * t.lda + 128);
+    __amdgpu_buffer_rsrc_t rb;
+    if (OPB_T) {
+      const int64_t nvalid = t.N - t.n0 < BN ? t.N - t.n0 : BN;
+      rb = rsrc_of(t.B + t.n0 * t.ldb + k0, (nvalid - 1) * t.ldb + 128);
+    } else {
+      rb = rsrc_of(t.B + k0 * t.ldb + t.n0, (t.K - k0) * t.ldb - t.n0);
+    }
+    const __amdgpu_buffer_rsrc_t rsa = rsrc_of(t.sA + (int64_t)g * t.sA_ld, t.rows * 4);
+    const __amdgpu_buffer_rsrc_t rsb =
+        rsrc_of(t.sB + (int64_t)g * t.sB_ld + (ROW128 ? t.n0 : 0), ROW128 ? (t.N - t.n0) * 4 : 4);
 #pragma unroll
-    for (int it = 0; it < BM / 64; ++it) {
-      const int64_t r = it * 64 + lane;
-      dma4(t.sA + (int64_t)g * t.sA_ld + (r < t.rows ? r : t.rows - 1), (uint8_t*)(sAs_buf + it * 64));
-    }
-  }
-  if (ROW128 && wave == NW - 1) {
+    for (int it = 0; it < CFG::A_ITERS; ++it)
+      dma16(ra, a, (int32_t)(it * 8 * NW * t.lda), buf + (it * NW + wave) * 1024);
 #pragma unroll
-    for (int it = 0; it < BN / 64; ++it) {
-      const int64_t n = t.n0 + it * 64 + lane;
-      dma4(t.sB + (int64_t)g * t.sB_ld + (n < t.N ? n : t.N - 1), (uint8_t*)(sBs_buf + it * 64));
+    for (int it = 0; it < CFG::B_ITERS; ++it) {
+      const int32_t so = OPB_T ? (int32_t)(it * 8 * NW * t.ldb) : (int32_t)(it * KSTEP * t.ldb);
+      dma16(rb, b, so, buf + CFG::A_BYTES + (it * NW + wave) * 1024);
     }
+    const int blk = wave < CFG::S_BLOCKS ? wave : 0;
+    dma4(sc_is_b ? rsb : rsa, sc, (uint8_t*)(sbuf + blk * 64));
   }
-}
+};
 
 template <class CFG, bool OPB_T, bool ROW128>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* lds) {
   constexpr int BM = CFG::BM, BN = CFG::BN;
   constexpr int TM = CFG::TM, TN = CFG::TN;
+  constexpr int S = CFG::STAGES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
   const int l16 = lane & 15, lq = lane >> 4;
 
-  float* sAs = reinterpret_cast<float*>(lds + 2 * CFG::BUF_BYTES);  // [2][BM]
-  float* sBs = sAs + 2 * BM;                                          // [2][BN] (ROW128)
+  // LDS: S operand buffers, then S scale buffers of BM + BN floats.
+  float* sbase = reinterpret_cast<float*>(lds + S * CFG::BUF_BYTES);
 
   const int G = (int)(t.K / 128);
   // Block-scale index of this wave's columns (uniform per wave).
   const int64_t nblk = (t.n0 + wn * CFG::WTN) / 128;
   const bool nblk_ok = nblk * 128 < t.N;
 
+  CopyPlan<CFG, OPB_T, ROW128> plan;
+  plan.init(t);
+
+  // acc[i][j] holds C[16*i + lane%16][16*j + 4*(lane/16) + r] of the wave's
+  // block: the MFMA computes C^T tiles (B fragment as the row operand), so a
+  // lane's four results share one row and one row scale.
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  issue_tile_loads<CFG, OPB_T, ROW128>(t, 0, lds, sAs, sBs);
+#pragma unroll
+  for (int s0 = 0; s0 < S - 1; ++s0)
+    if (s0 < G) plan.issue(t, s0, lds + s0 * CFG::BUF_BYTES, sbase + s0 * (BM + BN));
 
+  int cur = 0;
   for (int g = 0; g < G; ++g) {
-    const int cur = g & 1;
-    // Group g has landed in buffer `cur` once every lane's copies are done,
-    // and after the barrier every wave has finished reading the other buffer
-    // (group g-1): start group g+1's copies into it, then compute group g.
-    __builtin_amdgcn_s_waitcnt(0);
+    // Group g has landed in buffer `cur` once this wave's copies of it are
+    // complete (later groups may stay in flight); after the barrier every
+    // wave's copies are visible and every wave has finished reading the
+    // buffer of group g-1, which then receives group g+S-1.
+    if (g + S - 2 < G)
+      wait_vmcnt<(S - 2) * CFG::LOADS_PER_STAGE>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
-    if (g + 1 < G)
-      issue_tile_loads<CFG, OPB_T, ROW128>(t, g + 1, lds + (cur ^ 1) * CFG::BUF_BYTES, sAs + (cur ^ 1) * BM,
-                                           sBs + (cur ^ 1) * BN);
+    if (g + S - 1 < G) {
+      const int nb = cur == 0 ? S - 1 : cur - 1;
+      plan.issue(t, g + S - 1, lds + nb * CFG::BUF_BYTES, sbase + nb * (BM + BN));
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     const uint8_t* As = lds + cur * CFG::BUF_BYTES;
     const uint8_t* Bs = As + CFG::A_BYTES;
+    const float* sAc = sbase + cur * (BM + BN);
+    const float* sBc = sAc + BM;
 
-    // B scale for this group: block value (uniform) or per column.
-    float sbv[TN];
+    // Row scales of this lane's TM row tiles (contiguous by the copy plan).
+    float sa[TM];
+#pragma unroll
+    for (int i = 0; i < TM; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(sAc + wm * CFG::WTM + l16 * TM + i);
+      sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+    }
+    // Column scales: one block value per wave, or four per column tile.
+    float4 sbv[TN];
+    float sbb = 0.0f;
     if (ROW128) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sbv[j] = sBs[cur * BN + wn * CFG::WTN + 16 * j + l16];
+      for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sBc + wn * CFG::WTN + 16 * j + 4 * lq);
     } else {
-      const float sbb = nblk_ok ? (OPB_T ? t.sB[nblk * t.sB_ld + g] : t.sB[(int64_t)g * t.sB_ld + nblk]) : 0.0f;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sbv[j] = sbb;
+      sbb = nblk_ok ? (OPB_T ? t.sB[nblk * t.sB_ld + g] : t.sB[(int64_t)g * t.sB_ld + nblk]) : 0.0f;
     }
 
     // B fragments of this wave's TN column tiles.
@@ -231,40 +311,75 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* lds) {
       }
     }
 
+    // MFMAs of row tile i interleaved with the folds of row tile i-1, whose
+    // results are ready by then: one MFMA, then four FMAs (plus the scale
+    // multiply), so the matrix core and the vector ALU work side by side.
+    v4f pprev[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = wm * CFG::WTM + 16 * i + l16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq));
-      const uint4 hi = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq + 1));
-      const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const float4 sa = *reinterpret_cast<const float4*>(sAs + cur * BM + wm * CFG::WTM + 16 * i + 4 * lq);
-      v4f p[TN];
+    for (int i = 0; i <= TM; ++i) {
+      v4f pcur[TN];
+      if (i < TM) {
+        const int r = wm * CFG::WTM + 16 * i + l16;
+        const uint4 lo = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq));
+        const uint4 hi = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq + 1));
+        const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0,
-                                                                127, 0, 127);
+        for (int j = 0; j < TN; ++j)
+          pcur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0,
+                                                                     0, 0, 127, 0, 127);
+      }
+      if (i > 0) {
+        const int ip = i - 1;
+        if (ROW128) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        acc[i][j][0] = __builtin_fmaf(p[j][0], sa.x * sbv[j], acc[i][j][0]);
-        acc[i][j][1] = __builtin_fmaf(p[j][1], sa.y * sbv[j], acc[i][j][1]);
-        acc[i][j][2] = __builtin_fmaf(p[j][2], sa.z * sbv[j], acc[i][j][2]);
-        acc[i][j][3] = __builtin_fmaf(p[j][3], sa.w * sbv[j], acc[i][j][3]);
+          for (int j = 0; j < TN; ++j) {
+            acc[ip][j][0] = __builtin_fmaf(pprev[j][0] * sbv[j].x, sa[ip], acc[ip][j][0]);
+            acc[ip][j][1] = __builtin_fmaf(pprev[j][1] * sbv[j].y, sa[ip], acc[ip][j][1]);
+            acc[ip][j][2] = __builtin_fmaf(pprev[j][2] * sbv[j].z, sa[ip], acc[ip][j][2]);
+            acc[ip][j][3] = __builtin_fmaf(pprev[j][3] * sbv[j].w, sa[ip], acc[ip][j][3]);
+          }
+        } else {
+          const float sc = sa[ip] * sbb;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            acc[ip][j][0] = __builtin_fmaf(pprev[j][0], sc, acc[ip][j][0]);
+            acc[ip][j][1] = __builtin_fmaf(pprev[j][1], sc, acc[ip][j][1]);
+            acc[ip][j][2] = __builtin_fmaf(pprev[j][2], sc, acc[ip][j][2]);
+            acc[ip][j][3] = __builtin_fmaf(pprev[j][3], sc, acc[ip][j][3]);
+          }
+        }
+      }
+      if (i < TM) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) pprev[j] = pcur[j];
       }
     }
+    // Scheduling: alternate each MFMA with a group of vector instructions.
+#pragma unroll
+    for (int k = 0; k < TM * TN; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, ROW128 ? 8 : 5, 0);  // VALU (fold)
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               // 1 LDS read
+    }
     __builtin_amdgcn_sched_barrier(0);
+    cur = cur + 1 == S ? 0 : cur + 1;
   }
 
-  // ---- epilogue: FP32 C ----
+  // ---- epilogue: FP32 C, four consecutive columns per lane ----
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int64_t row = wm * CFG::WTM + 16 * i + l16;
+    if (row >= t.rows) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = wm * CFG::WTM + 16 * i + 4 * lq + r;
-      if (row >= t.rows) continue;
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = t.n0 + wn * CFG::WTN + 16 * j + 4 * lq;
+      float* dst = t.C + row * t.ldc + col;
+      if (col + 3 < t.N) {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = t.n0 + wn * CFG::WTN + 16 * j + l16;
-        if (col < t.N) t.C[row * t.ldc + col] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r)
+          if (col + r < t.N) dst[r] = acc[i][j][r];
       }
     }
   }
@@ -440,6 +555,9 @@ static fp8blk_status_t dispatch_dense(bool t, bool row, int64_t M, int64_t N, in
 
 using namespace fp8blk;
 
+// Per-lane copy offsets are 32-bit: operand pitches stay below 2^23 bytes.
+static constexpr int64_t kMaxPitch = int64_t(1) << 23;
+
 extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                                                        const float* sA, const uint8_t* B, int64_t ldb, int opB,
                                                        const float* sB, int bscale_mode, float* C, int64_t ldc,
@@ -454,6 +572,7 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
   if (K == 0) return FP8BLK_ERR_INVALID_ARG;
   if (!matrix_ok(A, M, K, lda, 1) || !matrix_ok(C, M, N, ldc, 4)) return FP8BLK_ERR_INVALID_ARG;
   if (opB == FP8BLK_OP_N ? !matrix_ok(B, K, N, ldb, 1) : !matrix_ok(B, N, K, ldb, 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (lda >= kMaxPitch || ldb >= kMaxPitch) return FP8BLK_ERR_UNSUPPORTED;
   const int64_t G = K / 128;
   const int64_t NB = ceil_div(N, 128);
   if (!vec_ok(sA, G * M)) return FP8BLK_ERR_INVALID_ARG;
@@ -492,6 +611,7 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   const int64_t Gk = K / 128, NB = ceil_div(N, 128);
   const int64_t brows = opB == FP8BLK_OP_N ? K : N, bcols = opB == FP8BLK_OP_N ? N : K;
   if (!matrix_ok(B, brows, bcols, ldb, 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (lda >= kMaxPitch || ldb >= kMaxPitch) return FP8BLK_ERR_UNSUPPORTED;
   if (strideB < brows * ldb || strideB % 16 != 0) return FP8BLK_ERR_INVALID_ARG;
   if (!vec_ok(sA, Gk * M_total) || !vec_ok(sB, Gk * NB)) return FP8BLK_ERR_INVALID_ARG;
   if (stride_sB < Gk * NB) return FP8BLK_ERR_INVALID_ARG;

@@ -142,7 +142,8 @@ fp8blk_status_t fp8blk_requantize_128x1_from_1x128(const uint8_t* q, const float
  *   B  [K][N] (opB = FP8BLK_OP_N, pitch ldb >= N) or [N][K] (FP8BLK_OP_T,
  *      pitch ldb >= K) E4M3 codes; sB per `bscale_mode`.
  *   C  [M][N] FP32, pitch ldc >= N (overwritten).
- *   K must be a positive multiple of 128 (M, N arbitrary).
+ *   K must be a positive multiple of 128 (M, N arbitrary); lda and ldb
+ *   must be below 2^23 (FP8BLK_ERR_UNSUPPORTED otherwise).
  *   Roles: Fprop Y = X W (A = 1x128-quantized X, B = W [K][N] block-scaled,
  *   OP_N); Dgrad dX = dY W^T (A = 1x128-quantized dY, B = the same W read as
  *   OP_T with its own block scales); Wgrad dW = X^T dY (A = 128x1-quantized
@@ -173,9 +174,9 @@ fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
  *   sB  G block-scale tables (BLOCK128 layout of one B_e), expert e at
  *       sB + e*stride_sB (floats).
  *   C   [M_total][N] FP32, pitch ldc.
- *   max_group_rows: an upper bound on any group's row count (e.g. M_total);
- *   it only sizes the launch grid.
- *   K must be a positive multiple of 128.
+ *   max_group_rows: an upper bound on any group's row count (e.g. M_total),
+ *   or 0 if unknown; it only sizes the launch grid.
+ *   K must be a positive multiple of 128; lda, ldb below 2^23.
  */
 fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(int64_t G, const int32_t* group_offsets,
                                                     int64_t M_total, int64_t max_group_rows,
