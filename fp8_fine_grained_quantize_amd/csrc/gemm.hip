@@ -16,9 +16,9 @@
 // 735329, p5 = inprokorea.com wr_id 890463).
 //
 // Data flow per workgroup tile (BM x BN), per K group:
-//   global -> LDS directly (global_load_lds_dwordx4, 16 bytes per lane),
-//     double buffered: group g+1 is copied while group g is computed; one
-//     barrier per group.
+//   global -> LDS directly (buffer_load_dwordx4 ... lds, 16 bytes per lane),
+//     double buffered in two distinct LDS arrays: group g+1 is copied while
+//     group g is computed; one barrier per group.
 //   LDS -> MFMA operands:
 //     K-major tiles (A, and B stored [N][K]): two ds_read_b128 per lane;
 //       16-byte chunks XOR-swizzled by row to spread LDS banks.
@@ -41,11 +41,11 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Workgroup tile: WAVES_M x WAVES_N waves, each owning TM x TN MFMA tiles of
-// 16x16; STAGES LDS buffers in the copy pipeline (group g+STAGES-1 is in
-// flight while group g is computed).
-template <int WAVES_M_, int WAVES_N_, int TM_, int TN_, int STAGES_>
+// 16x16.  Operands are double buffered in LDS: group g+1 is copied while
+// group g is computed.
+template <int WAVES_M_, int WAVES_N_, int TM_, int TN_>
 struct TileCfg {
-  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, TM = TM_, TN = TN_, STAGES = STAGES_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, TM = TM_, TN = TN_;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int WTM = 16 * TM, WTN = 16 * TN;
@@ -53,30 +53,32 @@ struct TileCfg {
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int A_CHUNKS = A_BYTES / 16, B_CHUNKS = B_BYTES / 16;
   static constexpr int A_ITERS = A_CHUNKS / (64 * NW), B_ITERS = B_CHUNKS / (64 * NW);
-  // Scale copies: BM floats of sA then BN floats of sB, 64 floats per wave
-  // instruction, spread so that every wave issues the same number of copies.
+  // Scale copies: BM floats of sA then BN floats of sB-side scales, 64
+  // floats per wave instruction, one instruction per wave.
   static constexpr int S_BLOCKS = (BM + BN) / 64;
-  static constexpr int S_ITERS = (S_BLOCKS + NW - 1) / NW;
-  static constexpr int LOADS_PER_STAGE = A_ITERS + B_ITERS + S_ITERS;  // per wave
   static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = STAGES * (BUF_BYTES + BM * 4 + BN * 4);
+  static constexpr int SC_FLOATS = BM + BN;
+  static constexpr int LDS_BYTES = 2 * (BUF_BYTES + SC_FLOATS * 4);
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must lie in one 128-column scale block");
   static_assert(BN >= 128, "the N-major swizzle needs BN >= 128");
   static_assert(A_CHUNKS % (64 * NW) == 0 && B_CHUNKS % (64 * NW) == 0, "whole 1 KB copy blocks per wave");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies in 64-float blocks");
-  static_assert(STAGES >= 2, "at least double buffering");
-  static_assert((STAGES - 2) * LOADS_PER_STAGE <= 63, "vmcnt range");
+  static_assert(S_BLOCKS <= NW, "one scale copy per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
 #ifndef FP8BLK_BIG_CFG
-#define FP8BLK_BIG_CFG 2, 4, 8, 4, 2  // 256 x 256 tile, 8 waves of 128 x 64, double buffered
+#define FP8BLK_BIG_CFG 2, 4, 8, 4  // 256 x 256 tile, 8 waves of 128 x 64
 #endif
 #ifndef FP8BLK_SMALL_CFG
-#define FP8BLK_SMALL_CFG 2, 2, 4, 4, 2  // 128 x 128 tile, 4 waves of 64 x 64
+#define FP8BLK_SMALL_CFG 2, 2, 4, 4  // 128 x 128 tile, 4 waves of 64 x 64
+#endif
+#ifndef FP8BLK_ROW_CFG
+#define FP8BLK_ROW_CFG 2, 2, 4, 4  // 128 x 128 tile, 4 waves of 64 x 64 (per-column scales need more registers)
 #endif
 using BigCfg = TileCfg<FP8BLK_BIG_CFG>;
 using SmallCfg = TileCfg<FP8BLK_SMALL_CFG>;
+using RowCfg = TileCfg<FP8BLK_ROW_CFG>;
 
 // s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -149,13 +151,11 @@ struct TileArgs {
 template <class CFG, bool OPB_T, bool ROW128>
 struct CopyPlan {
   static constexpr int NW = CFG::NW, BM = CFG::BM, BN = CFG::BN;
-  static_assert(CFG::S_ITERS == 1, "one scale copy per wave");
   // [K][N] B tile: BN/16 chunks per k row, so one copy iteration advances k
   // by KSTEP rows; the row swizzle (k & 7) must repeat across iterations.
   static constexpr int KSTEP = NW * 64 / (BN / 16);
   static_assert(KSTEP % 8 == 0, "[K][N] copies keep the row swizzle across iterations");
   uint32_t a, b, sc;
-  bool sc_is_b;  // uniform per wave
 
   __device__ __forceinline__ void init(const TileArgs& t) {
     constexpr int TM = CFG::TM, WTM = CFG::WTM;
@@ -176,193 +176,219 @@ struct CopyPlan {
     int blk = wave;
     if (blk >= CFG::S_BLOCKS) blk = 0;  // surplus copy: rewrites block 0 with the same data
     const int p = blk * 64 + lane;      // float position in the [BM + BN] scale buffer
-    if (p < BM) {
+    // BM is a multiple of 64, so the row/column choice is uniform per wave
+    // (derived from blk alone), which keeps the resource in scalar registers.
+    if (blk * 64 < BM) {
       const int w = p / WTM, q = p % WTM;
       sc = (uint32_t)((w * WTM + 16 * (q % TM) + q / TM) * 4);
-      sc_is_b = false;
+    } else if (ROW128) {
+      sc = (uint32_t)((p - BM) * 4);  // column scale of column n0 + (p - BM)
     } else {
-      sc = ROW128 ? (uint32_t)((p - BM) * 4) : 0u;  // block-scale mode: the half is unused
-      sc_is_b = ROW128;
+      // block scale of column block n0/128 + (p - BM); only the first BN/128
+      // positions are used
+      sc = (uint32_t)((p - BM) * (OPB_T ? t.K / 128 : 1) * 4);
     }
   }
 
   __device__ __forceinline__ void issue(const TileArgs& t, int g, uint8_t* buf, float* sbuf) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const Rsrc r = rsrc(t, g);
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) issue_one(r.a, r.b, r.sa, r.sb, n, t, buf, sbuf);
+  }
+
+  // Resources of group g's copies.
+  struct Rsrc {
+    __amdgpu_buffer_rsrc_t a, b, sa, sb;
+  };
+  __device__ __forceinline__ Rsrc rsrc(const TileArgs& t, int g) const {
     const int64_t k0 = (int64_t)g * 128;
-    const __amdgpu_buffer_rsrc_t ra = rsrc_of(t.A + k0, (t.rows - 1) * t.lda + 128);
-    __amdgpu_buffer_rsrc_t rb;
+    Rsrc r;
+    r.a = rsrc_of(t.A + k0, (t.rows - 1) * t.lda + 128);
     if (OPB_T) {
       const int64_t nvalid = t.N - t.n0 < BN ? t.N - t.n0 : BN;
-      rb = rsrc_of(t.B + t.n0 * t.ldb + k0, (nvalid - 1) * t.ldb + 128);
+      r.b = rsrc_of(t.B + t.n0 * t.ldb + k0, (nvalid - 1) * t.ldb + 128);
     } else {
-      rb = rsrc_of(t.B + k0 * t.ldb + t.n0, (t.K - k0) * t.ldb - t.n0);
+      r.b = rsrc_of(t.B + k0 * t.ldb + t.n0, (t.K - k0) * t.ldb - t.n0);
     }
-    const __amdgpu_buffer_rsrc_t rsa = rsrc_of(t.sA + (int64_t)g * t.sA_ld, t.rows * 4);
-    const __amdgpu_buffer_rsrc_t rsb =
-        rsrc_of(t.sB + (int64_t)g * t.sB_ld + (ROW128 ? t.n0 : 0), ROW128 ? (t.N - t.n0) * 4 : 4);
-#pragma unroll
-    for (int it = 0; it < CFG::A_ITERS; ++it)
+    r.sa = rsrc_of(t.sA + (int64_t)g * t.sA_ld, t.rows * 4);
+    if (ROW128) {
+      r.sb = rsrc_of(t.sB + (int64_t)g * t.sB_ld + t.n0, (t.N - t.n0) * 4);
+    } else {
+      const int64_t nb0 = t.n0 / 128, NB = (t.N + 127) / 128, Gk = t.K / 128;
+      r.sb = OPB_T ? rsrc_of(t.sB + nb0 * Gk + g, ((NB - nb0 - 1) * Gk + 1) * 4)
+                   : rsrc_of(t.sB + (int64_t)g * t.sB_ld + nb0, (NB - nb0) * 4);
+    }
+    return r;
+  }
+
+  // Copy number n (0 .. LOADS-1) of a group: A blocks, then B blocks, then
+  // the scale block.
+  static constexpr int LOADS = CFG::A_ITERS + CFG::B_ITERS + 1;
+  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb, int n,
+                                            const TileArgs& t, uint8_t* buf, float* sbuf) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (n < CFG::A_ITERS) {
+      const int it = n;
       dma16(ra, a, (int32_t)(it * 8 * NW * t.lda), buf + (it * NW + wave) * 1024);
-#pragma unroll
-    for (int it = 0; it < CFG::B_ITERS; ++it) {
+    } else if (n < CFG::A_ITERS + CFG::B_ITERS) {
+      const int it = n - CFG::A_ITERS;
       const int32_t so = OPB_T ? (int32_t)(it * 8 * NW * t.ldb) : (int32_t)(it * KSTEP * t.ldb);
       dma16(rb, b, so, buf + CFG::A_BYTES + (it * NW + wave) * 1024);
+    } else {
+      const int blk = wave < CFG::S_BLOCKS ? wave : 0;
+      if (blk * 64 < BM)
+        dma4(rsa, sc, (uint8_t*)(sbuf + blk * 64));
+      else
+        dma4(rsb, sc, (uint8_t*)(sbuf + blk * 64));
     }
-    const int blk = wave < CFG::S_BLOCKS ? wave : 0;
-    dma4(sc_is_b ? rsb : rsa, sc, (uint8_t*)(sbuf + blk * 64));
   }
 };
 
+// One K group of MFMAs and scale folds on operands already in LDS (`ops`:
+// A tile then B tile; `sc`: row scales in lane order, then column/block
+// scales).  acc[i][j] holds C[16*i + lane%16][16*j + 4*(lane/16) + r] of the
+// wave's block: the MFMA computes C^T tiles (B fragment as the row operand),
+// so a lane's four results share one row and one row scale.
 template <class CFG, bool OPB_T, bool ROW128>
-__device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* lds) {
-  constexpr int BM = CFG::BM, BN = CFG::BN;
-  constexpr int TM = CFG::TM, TN = CFG::TN;
-  constexpr int S = CFG::STAGES;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
+                                              v4f (&acc)[CFG::TM][CFG::TN]) {
+  constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
+  // The LDS addresses below are recomputed for every K group from an
+  // opaque copy of the thread index: held across the loop for both stages
+  // they would not fit in the register budget.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
   const int l16 = lane & 15, lq = lane >> 4;
+  const uint8_t* As = ops;
+  const uint8_t* Bs = ops + CFG::A_BYTES;
 
-  // LDS: S operand buffers, then S scale buffers of BM + BN floats.
-  float* sbase = reinterpret_cast<float*>(lds + S * CFG::BUF_BYTES);
+  // Row scales of this lane's TM row tiles (contiguous by the copy plan).
+  float sa[TM];
+#pragma unroll
+  for (int i = 0; i < TM; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
+    sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+  }
+  // Column scales: one block value per wave, or four per column tile.
+  float4 sbv[TN];
+  float sbb = 0.0f;
+  if (ROW128) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sc + BM + wn * CFG::WTN + 16 * j + 4 * lq);
+  } else {
+    sbb = sc[BM + (wn * CFG::WTN) / 128];
+  }
 
+  // B fragments of this wave's TN column tiles.
+  v8i bfr[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int ncol = wn * CFG::WTN + 16 * j;  // within the tile
+    if (OPB_T) {
+      const int r = ncol + l16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + kmaj_off(r, 2 * lq));
+      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + kmaj_off(r, 2 * lq + 1));
+      bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      const int jj = l16 >> 1, h = l16 & 1;
+      v2i part[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = 32 * lq + 8 * r + jj;
+        // 8-byte half h of 16-byte chunk (ncol/16) in row k
+        const int off = nmaj_off<BN>(k, ncol >> 4) + 8 * h;
+        part[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(Bs + off));
+      }
+      bfr[j] = v8i{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+    }
+  }
+
+  // Each MFMA's partial is folded right after the next MFMA has been issued
+  // (a two-entry ring), so the matrix core and the vector ALU can work side
+  // by side with only two partials live.  The next row tile's A fragment is
+  // read from LDS while the current row's MFMAs run.
+  auto load_a = [&](int i) {
+    const int r = wm * CFG::WTM + 16 * i + l16;
+    const uint4 lo = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq));
+    const uint4 hi = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq + 1));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto fold = [&](const v4f& p, int i, int j) {
+    if (ROW128) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sb = r == 0 ? sbv[j].x : r == 1 ? sbv[j].y : r == 2 ? sbv[j].z : sbv[j].w;
+        acc[i][j][r] = __builtin_fmaf(p[r] * sb, sa[i], acc[i][j][r]);
+      }
+    } else {
+      const float sc = sa[i] * sbb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sc, acc[i][j][r]);
+    }
+  };
+  v4f ring[2];
+  v8i afr = load_a(0);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int k = i * TN + j;
+      // C^T tile: the B fragment is the row operand.
+      ring[k & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0,
+                                                                     0, 127, 0, 127);
+      if (k > 0) fold(ring[(k - 1) & 1], (k - 1) / TN, (k - 1) % TN);
+    }
+    afr = anext;
+  }
+  fold(ring[(TM * TN - 1) & 1], TM - 1, TN - 1);
+}
+
+// The whole K loop of one output tile.  ops0/ops1 and sc0/sc1 are distinct
+// LDS arrays (the two pipeline stages); the loop is unrolled by two so that
+// every access names its array at compile time, which lets the compiler see
+// that reading one stage does not have to wait for copies into the other.
+template <class CFG, bool OPB_T, bool ROW128>
+__device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint8_t* ops1, float* sc0, float* sc1) {
+  constexpr int TM = CFG::TM, TN = CFG::TN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
+  const int l16 = lane & 15, lq = lane >> 4;
   const int G = (int)(t.K / 128);
-  // Block-scale index of this wave's columns (uniform per wave).
-  const int64_t nblk = (t.n0 + wn * CFG::WTN) / 128;
-  const bool nblk_ok = nblk * 128 < t.N;
 
   CopyPlan<CFG, OPB_T, ROW128> plan;
   plan.init(t);
 
-  // acc[i][j] holds C[16*i + lane%16][16*j + 4*(lane/16) + r] of the wave's
-  // block: the MFMA computes C^T tiles (B fragment as the row operand), so a
-  // lane's four results share one row and one row scale.
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-#pragma unroll
-  for (int s0 = 0; s0 < S - 1; ++s0)
-    if (s0 < G) plan.issue(t, s0, lds + s0 * CFG::BUF_BYTES, sbase + s0 * (BM + BN));
-
-  int cur = 0;
-  for (int g = 0; g < G; ++g) {
-    // Group g has landed in buffer `cur` once this wave's copies of it are
-    // complete (later groups may stay in flight); after the barrier every
-    // wave's copies are visible and every wave has finished reading the
-    // buffer of group g-1, which then receives group g+S-1.
-    if (g + S - 2 < G)
-      wait_vmcnt<(S - 2) * CFG::LOADS_PER_STAGE>();
-    else
-      wait_vmcnt<0>();
+  plan.issue(t, 0, ops0, sc0);
+  for (int g = 0; g < G; g += 2) {
+    // Group g has landed in stage 0 once this lane's copies are complete;
+    // after the barrier every wave's copies are visible and every wave is
+    // done reading stage 1 (group g-1), which then receives group g+1.
+    wait_vmcnt<0>();
     __syncthreads();
-    if (g + S - 1 < G) {
-      const int nb = cur == 0 ? S - 1 : cur - 1;
-      plan.issue(t, g + S - 1, lds + nb * CFG::BUF_BYTES, sbase + nb * (BM + BN));
-    }
+    if (g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
-
-    const uint8_t* As = lds + cur * CFG::BUF_BYTES;
-    const uint8_t* Bs = As + CFG::A_BYTES;
-    const float* sAc = sbase + cur * (BM + BN);
-    const float* sBc = sAc + BM;
-
-    // Row scales of this lane's TM row tiles (contiguous by the copy plan).
-    float sa[TM];
-#pragma unroll
-    for (int i = 0; i < TM; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(sAc + wm * CFG::WTM + l16 * TM + i);
-      sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
-    }
-    // Column scales: one block value per wave, or four per column tile.
-    float4 sbv[TN];
-    float sbb = 0.0f;
-    if (ROW128) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sBc + wn * CFG::WTN + 16 * j + 4 * lq);
-    } else {
-      sbb = nblk_ok ? (OPB_T ? t.sB[nblk * t.sB_ld + g] : t.sB[(int64_t)g * t.sB_ld + nblk]) : 0.0f;
-    }
-
-    // B fragments of this wave's TN column tiles.
-    v8i bfr[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int ncol = wn * CFG::WTN + 16 * j;  // within the tile
-      if (OPB_T) {
-        const int r = ncol + l16;
-        const uint4 lo = *reinterpret_cast<const uint4*>(Bs + kmaj_off(r, 2 * lq));
-        const uint4 hi = *reinterpret_cast<const uint4*>(Bs + kmaj_off(r, 2 * lq + 1));
-        bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      } else {
-        const int jj = l16 >> 1, h = l16 & 1;
-        v2i part[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int k = 32 * lq + 8 * r + jj;
-          // 8-byte half h of 16-byte chunk (ncol/16) in row k
-          const int off = nmaj_off<BN>(k, ncol >> 4) + 8 * h;
-          part[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(Bs + off));
-        }
-        bfr[j] = v8i{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
-      }
-    }
-
-    // MFMAs of row tile i interleaved with the folds of row tile i-1, whose
-    // results are ready by then: one MFMA, then four FMAs (plus the scale
-    // multiply), so the matrix core and the vector ALU work side by side.
-    v4f pprev[TN];
-#pragma unroll
-    for (int i = 0; i <= TM; ++i) {
-      v4f pcur[TN];
-      if (i < TM) {
-        const int r = wm * CFG::WTM + 16 * i + l16;
-        const uint4 lo = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq));
-        const uint4 hi = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq + 1));
-        const v8i afr = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          pcur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0,
-                                                                     0, 0, 127, 0, 127);
-      }
-      if (i > 0) {
-        const int ip = i - 1;
-        if (ROW128) {
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            acc[ip][j][0] = __builtin_fmaf(pprev[j][0] * sbv[j].x, sa[ip], acc[ip][j][0]);
-            acc[ip][j][1] = __builtin_fmaf(pprev[j][1] * sbv[j].y, sa[ip], acc[ip][j][1]);
-            acc[ip][j][2] = __builtin_fmaf(pprev[j][2] * sbv[j].z, sa[ip], acc[ip][j][2]);
-            acc[ip][j][3] = __builtin_fmaf(pprev[j][3] * sbv[j].w, sa[ip], acc[ip][j][3]);
-          }
-        } else {
-          const float sc = sa[ip] * sbb;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            acc[ip][j][0] = __builtin_fmaf(pprev[j][0], sc, acc[ip][j][0]);
-            acc[ip][j][1] = __builtin_fmaf(pprev[j][1], sc, acc[ip][j][1]);
-            acc[ip][j][2] = __builtin_fmaf(pprev[j][2], sc, acc[ip][j][2]);
-            acc[ip][j][3] = __builtin_fmaf(pprev[j][3], sc, acc[ip][j][3]);
-          }
-        }
-      }
-      if (i < TM) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) pprev[j] = pcur[j];
-      }
-    }
-    // Scheduling: alternate each MFMA with a group of vector instructions.
-#pragma unroll
-    for (int k = 0; k < TM * TN; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, ROW128 ? 8 : 5, 0);  // VALU (fold)
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               // 1 LDS read
-    }
+    compute_group<CFG, OPB_T, ROW128>(ops0, sc0, acc);
     __builtin_amdgcn_sched_barrier(0);
-    cur = cur + 1 == S ? 0 : cur + 1;
+    if (g + 1 < G) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_group<CFG, OPB_T, ROW128>(ops1, sc1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- epilogue: FP32 C, four consecutive columns per lane ----
@@ -384,6 +410,13 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* lds) {
     }
   }
 }
+
+// The two pipeline stages of a kernel, as distinct LDS arrays.
+#define FP8BLK_DECLARE_STAGES(CFG)                                   \
+  __shared__ __align__(16) uint8_t s_ops0[CFG::BUF_BYTES];           \
+  __shared__ __align__(16) uint8_t s_ops1[CFG::BUF_BYTES];           \
+  __shared__ __align__(16) float s_sc0[CFG::SC_FLOATS];              \
+  __shared__ __align__(16) float s_sc1[CFG::SC_FLOATS]
 
 // Map a linear workgroup id to a tile so that the workgroups placed on one
 // XCD (ids are dealt round-robin over the 8 XCDs) cover a contiguous run of
@@ -411,7 +444,7 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
                                                    const float* __restrict__ sB, int64_t sB_ld,
                                                    float* __restrict__ C, int64_t ldc, int64_t tiles_m,
                                                    int64_t tiles_n) {
-  extern __shared__ __align__(16) uint8_t lds[];
+  FP8BLK_DECLARE_STAGES(CFG);
   int64_t tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = tm * CFG::BM;
@@ -430,7 +463,7 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
   t.C = C + m0 * ldc;
   t.ldc = ldc;
   t.K = K;
-  gemm_tile<CFG, OPB_T, ROW128>(t, lds);
+  gemm_tile<CFG, OPB_T, ROW128>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Grouped: tiles are enumerated expert by expert, within an expert column
@@ -447,10 +480,9 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
                                                            int64_t strideB, const float* __restrict__ sB,
                                                            int64_t stride_sB, int64_t sB_ld,
                                                            float* __restrict__ C, int64_t ldc, int64_t tiles_n) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  // Scan scratch lives in the (not yet used) operand buffers.
-  int64_t* s_tile_base = reinterpret_cast<int64_t*>(lds);            // [NT + 1]
-  int64_t* s_found = s_tile_base + CFG::NT + 1;                      // [2]
+  FP8BLK_DECLARE_STAGES(CFG);
+  __shared__ int64_t s_tile_base[CFG::NT + 1];
+  __shared__ int64_t s_found[2];
   const int tid = threadIdx.x;
   // Linear tile id with the XCD remap.
   const int64_t nblocks = gridDim.x;
@@ -492,7 +524,6 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   }
   const int64_t e = s_found[0];
   const int64_t local = s_found[1];
-  __syncthreads();  // the scan scratch is about to be overwritten by tile data
   if (e < 0) return;  // surplus workgroup (uniform across the block)
   const int64_t r0 = offsets[e];
   const int64_t rows_e = (int64_t)offsets[e + 1] - r0;
@@ -515,16 +546,7 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   t.C = C + m0 * ldc;
   t.ldc = ldc;
   t.K = K;
-  gemm_tile<CFG, OPB_T, false>(t, lds);
-}
-
-// Dynamic LDS above the default limit must be allowed once per kernel; the
-// call configures the function, it does not allocate.
-template <class KERNEL>
-static void allow_lds(KERNEL k, int bytes) {
-  static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  static_cast<void>(once);
+  gemm_tile<CFG, OPB_T, false>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 template <class CFG, bool OPB_T, bool ROW128>
@@ -534,21 +556,17 @@ static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8
   const int64_t tiles_m = ceil_div(M, CFG::BM), tiles_n = ceil_div(N, CFG::BN);
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
-  auto kern = k_gemm<CFG, OPB_T, ROW128>;
-  allow_lds(kern, CFG::LDS_BYTES);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(CFG::NT), CFG::LDS_BYTES, stream, M, N, K, A, lda, sA, B,
+  hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128>), dim3((unsigned)blocks), dim3(CFG::NT), 0, stream, M, N, K, A, lda, sA, B,
                      ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n);
   return launch_status();
 }
 
-template <class CFG>
-static fp8blk_status_t dispatch_dense(bool t, bool row, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+template <class CFG, bool ROW128>
+static fp8blk_status_t dispatch_dense(bool t, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                                       int64_t lda, const float* sA, const uint8_t* B, int64_t ldb, const float* sB,
                                       int64_t sB_ld, float* C, int64_t ldc, hipStream_t st) {
-  if (t && row) return launch_dense<CFG, true, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
-  if (t) return launch_dense<CFG, true, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
-  if (row) return launch_dense<CFG, false, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
-  return launch_dense<CFG, false, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+  if (t) return launch_dense<CFG, true, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+  return launch_dense<CFG, false, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
 }
 
 }  // namespace fp8blk
@@ -585,13 +603,19 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
     sB_ld = opB == FP8BLK_OP_N ? NB : G;
   }
   hipStream_t st = as_stream(stream);
-  const bool t = opB == FP8BLK_OP_T, row = bscale_mode == FP8BLK_BSCALE_ROW128;
+  const bool t = opB == FP8BLK_OP_T;
   // 256x256 tiles when they give at least half a wave of workgroups over
   // the 256 CUs, 128x128 tiles otherwise.
+  if (bscale_mode == FP8BLK_BSCALE_ROW128) {
+    const int64_t row_tiles = ceil_div(M, RowCfg::BM) * ceil_div(N, RowCfg::BN);
+    if (row_tiles >= 128)
+      return dispatch_dense<RowCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+    return dispatch_dense<SmallCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+  }
   const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
   if (big_tiles >= 128)
-    return dispatch_dense<BigCfg>(t, row, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
-  return dispatch_dense<SmallCfg>(t, row, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+    return dispatch_dense<BigCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+  return dispatch_dense<SmallCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
 }
 
 extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
@@ -628,16 +652,11 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   if (blocks % 8) blocks += 8 - blocks % 8;  // keep the XCD remap a bijection on the grid
   if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
   hipStream_t st = as_stream(stream);
-  static_assert((CFG::NT + 3) * 8 <= CFG::BUF_BYTES, "scan scratch fits in the operand buffers");
   if (opB == FP8BLK_OP_T) {
-    auto kern = k_grouped_gemm<CFG, true>;
-    allow_lds(kern, CFG::LDS_BYTES);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(CFG::NT), CFG::LDS_BYTES, st, G, group_offsets, M_total, N,
+    hipLaunchKernelGGL((k_grouped_gemm<CFG, true>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G, group_offsets, M_total, N,
                        K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n);
   } else {
-    auto kern = k_grouped_gemm<CFG, false>;
-    allow_lds(kern, CFG::LDS_BYTES);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(CFG::NT), CFG::LDS_BYTES, st, G, group_offsets, M_total, N,
+    hipLaunchKernelGGL((k_grouped_gemm<CFG, false>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G, group_offsets, M_total, N,
                        K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n);
   }
   return launch_status();
