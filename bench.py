@@ -34,6 +34,15 @@ FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published (no sparsity)
 QUANT_BYTES_1X128 = 2 + 1 + 4 / 128       # per element: BF16 read, code write, scale per 128
 QUANT_BYTES_BLOCK = 2 + 1 + 4 / (128 * 128)
 
+# HBM traffic of one Fprop GEMM launch (4096 x 4096 x 7168, 256 x 256 tiles),
+# from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes over
+# `bench.py --steps 3 --warmup 1 --no-extras --no-cpu`, each scaled by what the
+# same counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0,
+# WRITE_SIZE x1.0).  Valid only for the GEMM source it was measured on
+# (sha256 below); reported as null otherwise.
+GEMM_TRAFFIC = {"sha256": "93bb0f0ddbbf708a234e3e8a3efac4eb26088ea5cbd24f7e2ae007f890a25935",
+                "fetch_bytes": 178317408, "write_bytes": 67108896}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -58,6 +67,16 @@ def calibrate_copy(torch):
     gbs = 2 * (1 << 30) / (t * 1e-3) / 1e9
     print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 1 << 30,
                       "bytes_written_per_launch": 1 << 30, "us": round(t * 1e3, 2), "GB/s": round(gbs, 1)}))
+
+
+def gemm_traffic():
+    """Measured HBM bytes per GEMM launch if the GEMM source is unchanged."""
+    import hashlib
+    src = os.path.join(ROOT, "fp8_fine_grained_quantize_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != GEMM_TRAFFIC["sha256"]:
+            return None
+    return GEMM_TRAFFIC["fetch_bytes"] + GEMM_TRAFFIC["write_bytes"]
 
 
 def timed_events(torch, fn, reps):
@@ -176,7 +195,8 @@ def main():
         "config": {"workload": "dense Fprop: q1x128(A[4096][7168]) + q128x128(W[7168][4096]) + FP8 GEMM 4096x4096x7168, FP32 out",
                    "M": M, "N": N, "K": K, "rotating_sets": S, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": gemm_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "gemm_fp8_blockscaled", "algorithmic": "2*M*N*K = 240.52 GFLOP per launch"},
         "kernels": kernels,
         "extras": extras,
@@ -275,16 +295,17 @@ def run_extras(torch, fb, synthetic, dev, np):
 
 def cpu_baseline(np, synthetic, A0, W0, M, N, K):
     """The oracle as it stands, on the host cores, on a bounded sample of the
-    step: 1x128 quantization of the first 512 rows of A, block quantization
-    of all of W, and the GEMM for those 512 rows (all 4096 columns).  Scaled
-    to TFLOP/s of the GEMM FLOPs covered by the sample."""
+    step: 1x128 quantization of the first 2048 rows of A, block quantization
+    of all of W, and the GEMM for those 2048 rows (all 4096 columns), about
+    5-10 s of host time.  Scaled to TFLOP/s of the GEMM FLOPs covered by the
+    sample."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = None
-    rows = 512
+    rows = 2048
     a_bits = synthetic.bf16_bits(A0[:rows])
     w_bits = synthetic.bf16_bits(W0)
     t0 = time.perf_counter()
