@@ -2,19 +2,20 @@
 
 A step is one pass of the dense Fprop path on the 4096 x 7168 x 4096 workload
 (DeepSeek-V3 hidden size 7168): 1x128 quantization of the activation
-A [4096][7168] (BF16 -> E4M3 + FP32 scales), 128x128 block quantization of
+A [4096][7168] (BF16 -> E4M3 + FP32 scales) and 128x128 block quantization of
 the weight W [7168][4096], and the block-scaled FP8 GEMM producing FP32
-C [4096][4096].  Inputs are seeded synthetic tensors already resident in HBM;
-the step rotates over several input/output sets whose total exceeds the
-256 MB Infinity Cache, so reads come from HBM.
+C [4096][4096], in order on one stream.
+Inputs are seeded synthetic tensors already resident in HBM; the step rotates
+over several input/output sets whose total exceeds the 256 MB Infinity Cache,
+so reads come from HBM.
 
 `value` = 2*M*N*K / step time (TFLOP/s of the whole step, quantizers
 included).  `roofline` reports the GEMM kernel alone (average duration from
 HIP events around each launch in the timed region) against the dense FP8
-MFMA peak.  `kernels` adds each kernel's time and roofline fraction, and
-`extras` times the other workloads' kernels (backward Dgrad/Wgrad, the
-accumulation study, the MoE grouped GEMMs).  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same step.
+MFMA peak.  `kernels` adds each kernel's time and roofline fraction (events
+between the step's kernels), and `extras` times the other workloads' kernels
+(backward Dgrad/Wgrad, the accumulation study, the MoE grouped GEMMs).
+`cpu_baseline` times the CPU oracle on a bounded sample of the step.
 
     python bench.py [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 """
@@ -81,7 +82,12 @@ def gemm_traffic():
 
 def timed_events(torch, fn, reps):
     """Average duration (ms) of fn() over reps launches, HIP events on the
-    current stream around each launch."""
+    current stream around each launch.  A sleep kernel queued first keeps the
+    GPU busy while the host enqueues the launches, so that each event pair
+    brackets GPU work only (short kernels would otherwise wait on the host)."""
+    fn(0)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(4_000_000)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     for i in range(reps):

@@ -83,44 +83,81 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// 128x128 blocks: one workgroup per block, 64 elements per lane held in
-// registers between the block-wide maximum and the encode.
+// 128x128 blocks, persistent and software-pipelined: a workgroup of NT lanes
+// takes blocks b, b + grid, ...; lane (sub = tid/16, c16 = tid%16) holds
+// chunk c16 of rows sub, sub + NT/16, ... (2048/NT chunks).  The next block's
+// loads are issued before the current block's maximum is reduced and its
+// codes are written.  The cross-wave maximum goes through one of two LDS
+// slots, alternating per block, so one barrier per block suffices.
 // ---------------------------------------------------------------------------
-template <bool POW2>
-__global__ __launch_bounds__(256) void k_quant_block128(const uint16_t* __restrict__ w, int64_t R, int64_t C,
-                                                         int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
-                                                         float* __restrict__ s, int64_t GC) {
-  __shared__ uint32_t red[4];
-  const int64_t bj = blockIdx.x, bi = blockIdx.y;
+template <bool POW2, int NT>
+__global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restrict__ w, int64_t R, int64_t C,
+                                                        int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ s, int64_t GR, int64_t GC) {
+  constexpr int CH = 2048 / NT, RSTEP = NT / 16, NWAVE = NT / 64;
+  __shared__ uint32_t red[2][NWAVE];
   const int sub = threadIdx.x >> 4;
   const int c16 = threadIdx.x & 15;
-  const int64_t col = bj * 128 + c16 * 8;
-  const int64_t avail = C - col;
+  const int64_t grid = gridDim.x;
+  const int64_t dbi = grid / GC, dbj = grid % GC;
+  int64_t bi = (int64_t)blockIdx.x / GC, bj = (int64_t)blockIdx.x % GC;
+  auto load = [&](int64_t i, int64_t j, uint4 (&v)[CH]) {
+    const int64_t col = j * 128 + c16 * 8;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t row = i * 128 + sub + RSTEP * c;
+      v[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < GR && row < R && col < C) v[c] = load_chunk8(w + row * ldw + col, C - col);
+    }
+  };
+  uint4 cur[CH], nxt[CH];
+  load(bi, bj, cur);
+  int par = 0;
+  while (bi < GR) {
+    int64_t ni = bi + dbi, nj = bj + dbj;
+    if (nj >= GC) {
+      nj -= GC;
+      ni += 1;
+    }
+    load(ni, nj, nxt);
+    uint32_t a = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) a = max(a, chunk_abs_max(cur[c]));
+    a = row16_max(a);
+    a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+    if ((threadIdx.x & 63) == 0) red[par][threadIdx.x >> 6] = a;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NWAVE; ++k) a = max(a, red[par][k]);
+    const TileScale ts = make_scale<POW2, true>(a << 16);
+    const int64_t col = bj * 128 + c16 * 8;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t row = bi * 128 + sub + RSTEP * c;
+      const uint2 codes = quantize8<POW2>(cur[c], ts);
+      if (row < R && col < C) store_chunk8(q + row * ldq + col, C - col, codes);
+    }
+    if (threadIdx.x == 0) s[bi * GC + bj] = ts.s;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) cur[c] = nxt[c];
+    bi = ni;
+    bj = nj;
+    par ^= 1;
+  }
+}
 
-  uint4 v[8];
-  uint32_t a = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = bi * 128 + sub + 16 * i;
-    v[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (row < R && avail > 0) v[i] = load_chunk8(w + row * ldw + col, avail);
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = max(a, chunk_abs_max(v[i]));
-  a = row16_max(a);
-  a = max(a, (uint32_t)__shfl_xor((int)a, 16));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 32));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-  __syncthreads();
-  a = max(max(red[0], red[1]), max(red[2], red[3]));
-  const TileScale ts = make_scale<POW2, true>(a << 16);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = bi * 128 + sub + 16 * i;
-    const uint2 codes = quantize8<POW2>(v[i], ts);
-    if (row < R && avail > 0) store_chunk8(q + row * ldq + col, avail, codes);
-  }
-  if (threadIdx.x == 0) s[bi * GC + bj] = ts.s;
+  return cus[dev];
 }
 
 // ---------------------------------------------------------------------------
@@ -396,12 +433,18 @@ extern "C" fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R
   const int64_t GR = ceil_div(R, 128), GC = ceil_div(C, 128);
   if (!vec_ok(s, GR * GC)) return FP8BLK_ERR_INVALID_ARG;
   if (R == 0 || C == 0) return FP8BLK_OK;
-  if (GC > 0x7FFFFFFF || GR > 65535) return FP8BLK_ERR_UNSUPPORTED;
-  const dim3 grid((unsigned)GC, (unsigned)GR);
+  // Persistent grid: 8 workgroups of 256 lanes per compute unit, each taking
+  // every grid-th block.
+  constexpr int NT = 256;
+  int64_t grid = GR * GC;
+  const int64_t cap = (int64_t)device_cus() * 8;
+  if (grid > cap) grid = cap;
   if (flags & FP8BLK_SCALE_POW2)
-    hipLaunchKernelGGL(k_quant_block128<true>, grid, dim3(256), 0, as_stream(stream), w, R, C, ldw, q, ldq, s, GC);
+    hipLaunchKernelGGL((k_quant_block128<true, NT>), dim3((unsigned)grid), dim3(NT), 0, as_stream(stream), w, R, C, ldw,
+                       q, ldq, s, GR, GC);
   else
-    hipLaunchKernelGGL(k_quant_block128<false>, grid, dim3(256), 0, as_stream(stream), w, R, C, ldw, q, ldq, s, GC);
+    hipLaunchKernelGGL((k_quant_block128<false, NT>), dim3((unsigned)grid), dim3(NT), 0, as_stream(stream), w, R, C,
+                       ldw, q, ldq, s, GR, GC);
   return launch_status();
 }
 
