@@ -189,14 +189,25 @@ def requantize_128x1_from_1x128(q: torch.Tensor, sq: torch.Tensor, pow2: bool = 
     return qT, sT
 
 
-def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCALE_BLOCK128, C=None):
+def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCALE_BLOCK128, C=None,
+                         split_k: bool = True, workspace=None):
     """C[M][N] float32 = block-scaled product of E4M3 codes A [M][K] and B
-    ([K][N] for OP_N, [N][K] for OP_T); see the header for scale layouts."""
+    ([K][N] for OP_N, [N][K] for OP_T); see the header for scale layouts.
+    With split_k, a workspace of workspace_bytes(M, N, K) bytes is passed
+    (allocated here unless given), which lets the library split K on shapes
+    whose tiles cannot fill the GPU."""
     M, K = A.shape
     N = B.shape[1] if opB == OP_N else B.shape[0]
     C = _empty_pitched(M, N, torch.float32, A.device, 4) if C is None else C
+    ws_ptr, ws_bytes = None, 0
+    if split_k and M and N and K:
+        need = workspace_bytes(M, N, K, 1)
+        if need:
+            if workspace is None:
+                workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=A.device)
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check(lib().fp8blk_gemm_fp8_blockscaled(M, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), _pitch(B), opB,
-                                             _ptr(sB), bscale_mode, _ptr(C), _pitch(C), None, 0, _stream()),
+                                             _ptr(sB), bscale_mode, _ptr(C), _pitch(C), ws_ptr, ws_bytes, _stream()),
            "gemm_fp8_blockscaled")
     return C
 

@@ -1,5 +1,4 @@
-// Small host-only entry points of libfp8blk: status names, ABI version and the
-// scratch-size query.
+// Small host-only entry points of libfp8blk: status names and ABI version.
 #include "host_common.h"
 
 extern "C" const char* fp8blk_status_string(fp8blk_status_t status) {
@@ -14,7 +13,3 @@ extern "C" const char* fp8blk_status_string(fp8blk_status_t status) {
 
 extern "C" int fp8blk_abi_version(void) { return 1; }
 
-extern "C" size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G) {
-  (void)M; (void)N; (void)K; (void)G;
-  return 0;
-}

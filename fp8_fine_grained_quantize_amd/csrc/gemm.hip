@@ -142,6 +142,7 @@ struct TileArgs {
   float* C;           // C + m0 * ldc
   int64_t ldc;
   int64_t K;
+  int g0, g1;         // K groups [g0, g1) of this tile's (partial) product
 };
 
 // Copies of one K group.  Group bases: A tile A + k0; B tile B + n0*ldb + k0
@@ -359,7 +360,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
   const int wave = threadIdx.x >> 6;
   const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int G = (int)(t.K / 128);
+  const int g0 = t.g0, G = t.g1;
 
   CopyPlan<CFG, OPB_T, ROW128> plan;
   plan.init(t);
@@ -370,8 +371,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  plan.issue(t, 0, ops0, sc0);
-  for (int g = 0; g < G; g += 2) {
+  plan.issue(t, g0, ops0, sc0);
+  for (int g = g0; g < G; g += 2) {
     // Group g has landed in stage 0 once this lane's copies are complete;
     // after the barrier every wave's copies are visible and every wave is
     // done reading stage 1 (group g-1), which then receives group g+1.
@@ -443,10 +444,18 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
                                                    const uint8_t* __restrict__ B, int64_t ldb,
                                                    const float* __restrict__ sB, int64_t sB_ld,
                                                    float* __restrict__ C, int64_t ldc, int64_t tiles_m,
-                                                   int64_t tiles_n) {
+                                                   int64_t tiles_n, float* __restrict__ partials, int groups_per_split) {
   FP8BLK_DECLARE_STAGES(CFG);
   int64_t tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  // Split K: workgroup row blockIdx.y computes the partial product of K
+  // groups [y*groups_per_split, ...) into its own [M][N] slice of `partials`.
+  const int G = (int)(K / 128);
+  const int split = blockIdx.y;
+  if (gridDim.y > 1) {
+    C = partials + (int64_t)split * M * N;
+    ldc = N;
+  }
   const int64_t m0 = tm * CFG::BM;
   TileArgs t;
   t.A = A + m0 * lda;
@@ -463,6 +472,8 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
   t.C = C + m0 * ldc;
   t.ldc = ldc;
   t.K = K;
+  t.g0 = split * groups_per_split;
+  t.g1 = t.g0 + groups_per_split < G ? t.g0 + groups_per_split : G;
   gemm_tile<CFG, OPB_T, ROW128>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
@@ -546,27 +557,86 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   t.C = C + m0 * ldc;
   t.ldc = ldc;
   t.K = K;
+  t.g0 = 0;
+  t.g1 = (int)(K / 128);
   gemm_tile<CFG, OPB_T, false>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+}
+
+// Split-K reduction: C[m][n] = sum over s = 0 .. S-1, in that order, of the
+// partial products partials[s][m][n] (FP32 additions).  Four consecutive
+// columns per thread.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partials, int S, int64_t M,
+                                                       int64_t N, float* __restrict__ C, int64_t ldc) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index of a 4-column chunk
+  const int64_t cpr = (N + 3) / 4;
+  const int64_t m = q / cpr, n = (q % cpr) * 4;
+  if (m >= M) return;
+  const int64_t MN = M * N;
+  const float* src = partials + m * N + n;
+  float* dst = C + m * ldc + n;
+  if (n + 4 <= N && (N & 3) == 0) {
+    float4 acc = *reinterpret_cast<const float4*>(src);
+    for (int s = 1; s < S; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(src + s * MN);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(dst) = acc;
+  } else {
+    for (int r = 0; r < 4 && n + r < N; ++r) {
+      float acc = src[r];
+      for (int s = 1; s < S; ++s) acc += src[s * MN + r];
+      dst[r] = acc;
+    }
+  }
+}
+
+// K splits for a dense GEMM: only when its 128 x 128 tiles cannot fill the
+// compute units; each split keeps at least four K groups.
+static int64_t splitk_count(int64_t M, int64_t N, int64_t K) {
+  const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
+  if (big_tiles >= 128) return 1;
+  const int64_t tiles = ceil_div(M, SmallCfg::BM) * ceil_div(N, SmallCfg::BN);
+  const int64_t slots = 2 * (int64_t)device_cus();  // two 128 x 128 workgroups fit per CU
+  int64_t S = ceil_div(slots, tiles);
+  const int64_t G = K / 128;
+  if (S > G / 4) S = G / 4;
+  if (S > 16) S = 16;
+  return S < 1 ? 1 : S;
+}
+
+static size_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
+  const int64_t S = splitk_count(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 template <class CFG, bool OPB_T, bool ROW128>
 static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
                                     const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_ld, float* C,
-                                    int64_t ldc, hipStream_t stream) {
+                                    int64_t ldc, float* partials, int64_t S, hipStream_t stream) {
   const int64_t tiles_m = ceil_div(M, CFG::BM), tiles_n = ceil_div(N, CFG::BN);
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128>), dim3((unsigned)blocks), dim3(CFG::NT), 0, stream, M, N, K, A, lda, sA, B,
-                     ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n);
+  const int64_t G = K / 128;
+  const int64_t per = ceil_div(G, S);
+  S = ceil_div(G, per);  // no empty split
+  hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128>), dim3((unsigned)blocks, (unsigned)S), dim3(CFG::NT), 0, stream, M, N,
+                     K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per);
+  if (S > 1) {
+    if (hipGetLastError() != hipSuccess) return FP8BLK_ERR_LAUNCH;
+    const int64_t chunks = M * ceil_div(N, 4);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(chunks, 256)), dim3(256), 0, stream, partials, (int)S,
+                       M, N, C, ldc);
+  }
   return launch_status();
 }
 
 template <class CFG, bool ROW128>
 static fp8blk_status_t dispatch_dense(bool t, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                                       int64_t lda, const float* sA, const uint8_t* B, int64_t ldb, const float* sB,
-                                      int64_t sB_ld, float* C, int64_t ldc, hipStream_t st) {
-  if (t) return launch_dense<CFG, true, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
-  return launch_dense<CFG, false, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+                                      int64_t sB_ld, float* C, int64_t ldc, float* partials, int64_t S,
+                                      hipStream_t st) {
+  if (t) return launch_dense<CFG, true, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+  return launch_dense<CFG, false, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
 }
 
 }  // namespace fp8blk
@@ -576,12 +646,17 @@ using namespace fp8blk;
 // Per-lane copy offsets are 32-bit: operand pitches stay below 2^23 bytes.
 static constexpr int64_t kMaxPitch = int64_t(1) << 23;
 
+// Workspace that lets the dense GEMM split K (0: it never splits this
+// shape); the grouped GEMM needs none.
+extern "C" size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G) {
+  if (G > 1 || M <= 0 || N <= 0 || K <= 0 || K % 128 != 0) return 0;
+  return splitk_bytes(M, N, K);
+}
+
 extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                                                        const float* sA, const uint8_t* B, int64_t ldb, int opB,
                                                        const float* sB, int bscale_mode, float* C, int64_t ldc,
                                                        void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (M < 0 || N < 0 || K < 0) return FP8BLK_ERR_INVALID_ARG;
   if (opB != FP8BLK_OP_N && opB != FP8BLK_OP_T) return FP8BLK_ERR_INVALID_ARG;
   if (bscale_mode != FP8BLK_BSCALE_BLOCK128 && bscale_mode != FP8BLK_BSCALE_ROW128) return FP8BLK_ERR_INVALID_ARG;
@@ -604,18 +679,28 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
   }
   hipStream_t st = as_stream(stream);
   const bool t = opB == FP8BLK_OP_T;
+  // Split K when a large enough workspace is given and the tiles alone
+  // cannot fill the GPU; otherwise one pass writes C directly.
+  int64_t S = splitk_count(M, N, K);
+  float* partials = nullptr;
+  if (S > 1) {
+    if (workspace != nullptr && workspace_bytes >= splitk_bytes(M, N, K) && aligned(workspace, 16))
+      partials = static_cast<float*>(workspace);
+    else
+      S = 1;
+  }
   // 256x256 tiles when they give at least half a wave of workgroups over
   // the 256 CUs, 128x128 tiles otherwise.
   if (bscale_mode == FP8BLK_BSCALE_ROW128) {
     const int64_t row_tiles = ceil_div(M, RowCfg::BM) * ceil_div(N, RowCfg::BN);
     if (row_tiles >= 128)
-      return dispatch_dense<RowCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
-    return dispatch_dense<SmallCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+      return dispatch_dense<RowCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+    return dispatch_dense<SmallCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
   }
   const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
   if (big_tiles >= 128)
-    return dispatch_dense<BigCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
-  return dispatch_dense<SmallCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, st);
+    return dispatch_dense<BigCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+  return dispatch_dense<SmallCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
 }
 
 extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(

@@ -147,18 +147,6 @@ __global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restric
   }
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 // ---------------------------------------------------------------------------
 // 128x1 with transposed output: one workgroup per 128 tokens x 128 channels.

@@ -149,8 +149,15 @@ fp8blk_status_t fp8blk_requantize_128x1_from_1x128(const uint8_t* q, const float
  *   OP_T with its own block scales); Wgrad dW = X^T dY (A = 128x1-quantized
  *   X as [d_in][T], B = 128x1-quantized dY as [d_out][T] with OP_T and
  *   FP8BLK_BSCALE_ROW128) [p1¶3; p5¶4].
- *   workspace / workspace_bytes: reserved for split-K partials; pass NULL/0
- *   (fp8blk_workspace_bytes returns 0 for every shape in this version).
+ *   workspace / workspace_bytes: optional DEVICE scratch (16-byte aligned,
+ *   owned by the caller, contents on entry irrelevant) of at least
+ *   fp8blk_workspace_bytes(M, N, K, 1) bytes.  When the shape's output
+ *   tiles are too few to fill the GPU and such a workspace is given, K is
+ *   split into S ranges of whole groups: each range's partial product
+ *   (formed exactly as above) goes to the workspace and C is their sum in
+ *   range order (S-1 extra FP32 additions per element; deterministic).
+ *   NULL/0 (or a smaller workspace) computes C in one pass.  The workspace
+ *   must not be used by other work on other streams during the call.
  */
 fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                             const uint8_t* A, int64_t lda, const float* sA,
@@ -188,7 +195,9 @@ fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(int64_t G, const int32_t* gr
                                                     void* workspace, size_t workspace_bytes,
                                                     void* stream);
 
-/* Scratch bytes the GEMMs need for the given shape (0: none needed). */
+/* Workspace that lets fp8blk_gemm_fp8_blockscaled split K for this shape
+ * (G = 1), for the current device; 0 when it would not split.  The grouped
+ * GEMM (G > 1) needs none. */
 size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
 
 /* Human-readable name of a status code (static string). */

@@ -41,7 +41,11 @@ def test_version_and_status_strings():
     assert fb.status_string(1) == "FP8BLK_ERR_INVALID_ARG"
     assert fb.status_string(2) == "FP8BLK_ERR_UNSUPPORTED"
     assert fb.status_string(3) == "FP8BLK_ERR_LAUNCH"
-    assert fb.workspace_bytes(4096, 4096, 7168, 1) == 0
+    assert fb.workspace_bytes(4096, 4096, 7168, 1) == 0      # tiles fill the GPU: no split
+    ws = fb.workspace_bytes(1024, 1024, 4096, 1)              # 64 tiles: K is split
+    assert ws > 0 and ws % (1024 * 1024 * 4) == 0 and 2 <= ws // (1024 * 1024 * 4) <= 16
+    assert fb.workspace_bytes(1024, 1024, 4096, 8) == 0       # grouped: none
+    assert fb.workspace_bytes(1024, 1024, 256, 1) == 0        # two K groups: no split
 
 
 P = ctypes.c_void_p

@@ -120,6 +120,40 @@ def test_pow2_rescaling_and_determinism():
     assert np.array_equal(C3, (C1 * np.float32(2.0 ** 7)).astype(np.float32))
 
 
+@pytest.mark.parametrize("opB,mode", CASES)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 2048), (300, 200, 1024), (64, 1000, 4096)])
+def test_split_k(M, N, K, opB, mode):
+    """Shapes with too few tiles to fill the GPU split K over a workspace:
+    the result still meets the oracle gate, stays within a few FP32 ulps of
+    the one-pass result (S-1 extra additions), and is deterministic."""
+    assert fb.workspace_bytes(M, N, K, 1) > 0
+    g = torch.Generator().manual_seed(M + N + K)
+    A = synthetic.randn_bf16((M, K), 1.0, g)
+    if opB == oracle.OP_N:
+        B = synthetic.randn_bf16((K, N), 0.02, g)
+        qA, sA = oracle.quantize_1x128(bf16_bits(A))
+        if mode == oracle.BSCALE_BLOCK128:
+            qB, sB = oracle.quantize_block128(bf16_bits(B))
+        else:  # 128-deep tiles along K per column: 128x1 of B [K][N], codes back in [K][N]
+            qBT, sB = oracle.quantize_128x1(bf16_bits(B))
+            qB = np.ascontiguousarray(qBT.T)
+    else:
+        B = synthetic.randn_bf16((N, K), 0.02, g)
+        qA, sA = oracle.quantize_1x128(bf16_bits(A))
+        qB, sB = (oracle.quantize_block128(bf16_bits(B)) if mode == oracle.BSCALE_BLOCK128 else
+                  oracle.quantize_1x128(bf16_bits(B)))
+    dev = [u8_dev(qA), f32_dev(sA), u8_dev(qB), f32_dev(sB)]
+    print(f"[gemm] split-K {M}x{N}x{K} opB={opB} mode={mode}", flush=True)
+    C1 = np_f32(fb.gemm_fp8_blockscaled(*dev, opB=opB, bscale_mode=mode, split_k=False))
+    Cs = np_f32(fb.gemm_fp8_blockscaled(*dev, opB=opB, bscale_mode=mode))
+    Cs2 = np_f32(fb.gemm_fp8_blockscaled(*dev, opB=opB, bscale_mode=mode))
+    torch.cuda.synchronize()
+    R = oracle.gemm_blockscaled(qA, sA, qB, sB, opB, mode)
+    assert e_norm(Cs, R) <= 1e-3
+    assert np.array_equal(Cs.view(np.uint32), Cs2.view(np.uint32))
+    assert float(np.max(np.abs(Cs.astype(np.float64) - C1)) / np.max(np.abs(R))) <= 1e-5
+
+
 def _sampled(C, qA, sA, qB, sB, opB, mode, n=4096, seed=0):
     rng = np.random.default_rng(seed)
     M, N = C.shape

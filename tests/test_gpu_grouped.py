@@ -49,7 +49,8 @@ def test_grouped_small(opB, counts):
         r0, r1 = off[e], off[e + 1]
         if r1 == r0:
             continue
-        Cd = fb.gemm_fp8_blockscaled(u8_dev(qA[r0:r1]), f32_dev(sA[:, r0:r1]), u8_dev(B[e]), f32_dev(sB[e]), opB=opB)
+        Cd = fb.gemm_fp8_blockscaled(u8_dev(qA[r0:r1]), f32_dev(sA[:, r0:r1]), u8_dev(B[e]), f32_dev(sB[e]), opB=opB,
+                                     split_k=False)
         torch.cuda.synchronize()
         assert np.array_equal(np_f32(Cd).view(np.uint32), Cg[r0:r1].view(np.uint32)), f"expert {e}"
 
