@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "Fp8BlkError", "lib", "library_path", "OP_N", "OP_T", "BSCALE_BLOCK128", "BSCALE_ROW128",
-    "SCALE_POW2", "quantize_1x128", "quantize_128x1", "quantize_block128",
+    "SCALE_POW2", "GEMM_POW2_SCALES", "quantize_1x128", "quantize_128x1", "quantize_block128",
     "requantize_128x1_from_1x128", "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled",
     "workspace_bytes", "status_string", "abi_version", "EXPORTED_SYMBOLS", "empty_pitched", "as_pitched",
 ]
@@ -26,6 +26,7 @@ __all__ = [
 OP_N, OP_T = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 SCALE_POW2 = 0x1
+GEMM_POW2_SCALES = 0x100   # OR into opB: every scale is a power of two
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
 
@@ -190,12 +191,13 @@ def requantize_128x1_from_1x128(q: torch.Tensor, sq: torch.Tensor, pow2: bool = 
 
 
 def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCALE_BLOCK128, C=None,
-                         split_k: bool = True, workspace=None):
+                         split_k: bool = True, workspace=None, pow2_scales: bool = False):
     """C[M][N] float32 = block-scaled product of E4M3 codes A [M][K] and B
     ([K][N] for OP_N, [N][K] for OP_T); see the header for scale layouts.
     With split_k, a workspace of workspace_bytes(M, N, K) bytes is passed
     (allocated here unless given), which lets the library split K on shapes
-    whose tiles cannot fill the GPU."""
+    whose tiles cannot fill the GPU.  pow2_scales asserts that every scale is
+    a power of two (GEMM_POW2_SCALES)."""
     M, K = A.shape
     N = B.shape[1] if opB == OP_N else B.shape[0]
     C = _empty_pitched(M, N, torch.float32, A.device, 4) if C is None else C
@@ -206,13 +208,15 @@ def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCAL
             if workspace is None:
                 workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=A.device)
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
-    _check(lib().fp8blk_gemm_fp8_blockscaled(M, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), _pitch(B), opB,
-                                             _ptr(sB), bscale_mode, _ptr(C), _pitch(C), ws_ptr, ws_bytes, _stream()),
+    _check(lib().fp8blk_gemm_fp8_blockscaled(M, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), _pitch(B),
+                                             opB | (GEMM_POW2_SCALES if pow2_scales else 0), _ptr(sB), bscale_mode,
+                                             _ptr(C), _pitch(C), ws_ptr, ws_bytes, _stream()),
            "gemm_fp8_blockscaled")
     return C
 
 
-def grouped_gemm_fp8_blockscaled(offsets, A, sA, B, sB, opB: int = OP_N, max_group_rows=None, C=None):
+def grouped_gemm_fp8_blockscaled(offsets, A, sA, B, sB, opB: int = OP_N, max_group_rows=None, C=None,
+                                 pow2_scales: bool = False):
     """Per-expert GEMM.  offsets: device int32 [G+1]; A [M_total][K];
     B [G][K][N] (OP_N) or [G][N][K] (OP_T) contiguous per expert; sB [G][...]."""
     G = offsets.numel() - 1
@@ -223,6 +227,7 @@ def grouped_gemm_fp8_blockscaled(offsets, A, sA, B, sB, opB: int = OP_N, max_gro
     C = _empty_pitched(M, N, torch.float32, A.device, 4) if C is None else C
     mgr = M if max_group_rows is None else int(max_group_rows)
     _check(lib().fp8blk_grouped_gemm_fp8_blockscaled(
-        G, _ptr(offsets), M, mgr, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), B.stride(1), B.stride(0), opB,
+        G, _ptr(offsets), M, mgr, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), B.stride(1), B.stride(0),
+        opB | (GEMM_POW2_SCALES if pow2_scales else 0),
         _ptr(sB), sB.stride(0), _ptr(C), _pitch(C), None, 0, _stream()), "grouped_gemm_fp8_blockscaled")
     return C

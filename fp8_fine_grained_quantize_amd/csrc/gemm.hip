@@ -11,6 +11,12 @@
 // starting from zero), and the FP32 result is folded into a separate FP32
 // accumulator with one FMA by fl32(sA * sB).  Fprop, Dgrad and Wgrad all use
 // this kernel family [p1¶3, Figure 6; p5¶4].
+//
+// When every scale is a power of two (the pages' choice for some activations
+// [p2¶4]; FP8BLK_GEMM_POW2_SCALES), the scales are exact E8M0 block scales:
+// the MFMA applies them to its operands and adds the group's product to the
+// FP32 accumulator itself (srcC, round to nearest even), so the promotion
+// needs no vector-ALU work.
 // Citations [pN¶k]: N-th page of the source collection, k-th paragraph
 // (p1 = xn--9g3bo1gtkw0l8ubf92bgle.kr wr_id 85187, p2 = inprokorea.com wr_id
 // 735329, p5 = inprokorea.com wr_id 890463).
@@ -251,7 +257,36 @@ struct CopyPlan {
 // scales).  acc[i][j] holds C[16*i + lane%16][16*j + 4*(lane/16) + r] of the
 // wave's block: the MFMA computes C^T tiles (B fragment as the row operand),
 // so a lane's four results share one row and one row scale.
-template <class CFG, bool OPB_T, bool ROW128>
+// MFMA with E8M0 block scales: byte OA of `sa` scales the rows of the first
+// operand, byte OB of `sb` those of the second (lane l supplies the scale of
+// row l%16 for its 32-deep k block l/16); srcC is accumulated in FP32.
+template <int OA, int OB>
+__device__ __forceinline__ v4f mfma_e8m0(const v8i& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, OA, sa, OB, sb);
+}
+template <int OA>
+__device__ __forceinline__ v4f mfma_e8m0_b(int ob, const v8i& a, const v8i& b, const v4f& c, uint32_t sa,
+                                           uint32_t sb) {
+  switch (ob & 3) {
+    case 0: return mfma_e8m0<OA, 0>(a, b, c, sa, sb);
+    case 1: return mfma_e8m0<OA, 1>(a, b, c, sa, sb);
+    case 2: return mfma_e8m0<OA, 2>(a, b, c, sa, sb);
+    default: return mfma_e8m0<OA, 3>(a, b, c, sa, sb);
+  }
+}
+__device__ __forceinline__ v4f mfma_e8m0_sel(int oa, int ob, const v8i& a, const v8i& b, const v4f& c, uint32_t sa,
+                                             uint32_t sb) {
+  switch (oa & 3) {
+    case 0: return mfma_e8m0_b<0>(ob, a, b, c, sa, sb);
+    case 1: return mfma_e8m0_b<1>(ob, a, b, c, sa, sb);
+    case 2: return mfma_e8m0_b<2>(ob, a, b, c, sa, sb);
+    default: return mfma_e8m0_b<3>(ob, a, b, c, sa, sb);
+  }
+}
+// E8M0 code of a power-of-two FP32 scale: its biased exponent.
+__device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
+
+template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
                                               v4f (&acc)[CFG::TM][CFG::TN]) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
@@ -308,16 +343,48 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
     }
   }
 
-  // Each MFMA's partial is folded right after the next MFMA has been issued
-  // (a two-entry ring), so the matrix core and the vector ALU can work side
-  // by side with only two partials live.  The next row tile's A fragment is
-  // read from LDS while the current row's MFMAs run.
   auto load_a = [&](int i) {
     const int r = wm * CFG::WTM + 16 * i + l16;
     const uint4 lo = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq));
     const uint4 hi = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq + 1));
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
+  static_assert(!(P2 && ROW128) || TN <= 4, "four column tiles per packed scale register");
+  if (P2) {
+    // Power-of-two scales applied by the matrix core: E8M0 exponents of the
+    // TM row scales, four per register (byte i%4 for row tile i), and of the
+    // column scales (four column tiles per register, byte j) or the block
+    // scale; each group's product is added to the FP32 accumulator by the
+    // MFMA itself.
+    uint32_t sae[(TM + 3) / 4];
+#pragma unroll
+    for (int q = 0; q < (TM + 3) / 4; ++q) sae[q] = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sae[i / 4] |= e8m0_of(sa[i]) << (8 * (i % 4));
+    uint32_t sbe = 0;
+    if (ROW128) {
+#pragma unroll
+      for (int j = 0; j < TN && j < 4; ++j)
+        sbe |= e8m0_of(sc[BM + wn * CFG::WTN + 16 * j + l16]) << (8 * j);
+    } else {
+      sbe = e8m0_of(sbb);
+    }
+    v8i afr = load_a(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = mfma_e8m0_sel(ROW128 ? j : 0, i % 4, bfr[j], afr, acc[i][j], sbe, sae[i / 4]);
+      afr = anext;
+    }
+    return;
+  }
+
+  // Each MFMA's partial is folded right after the next MFMA has been issued
+  // (a two-entry ring), so the matrix core and the vector ALU can work side
+  // by side with only two partials live.  The next row tile's A fragment is
+  // read from LDS while the current row's MFMAs run.
   auto fold = [&](const v4f& p, int i, int j) {
     if (ROW128) {
 #pragma unroll
@@ -353,7 +420,7 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
 // LDS arrays (the two pipeline stages); the loop is unrolled by two so that
 // every access names its array at compile time, which lets the compiler see
 // that reading one stage does not have to wait for copies into the other.
-template <class CFG, bool OPB_T, bool ROW128>
+template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint8_t* ops1, float* sc0, float* sc1) {
   constexpr int TM = CFG::TM, TN = CFG::TN;
   const int lane = threadIdx.x & 63;
@@ -380,14 +447,14 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     __syncthreads();
     if (g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_group<CFG, OPB_T, ROW128>(ops0, sc0, acc);
+    compute_group<CFG, OPB_T, ROW128, P2>(ops0, sc0, acc);
     __builtin_amdgcn_sched_barrier(0);
     if (g + 1 < G) {
       wait_vmcnt<0>();
       __syncthreads();
       if (g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group<CFG, OPB_T, ROW128>(ops1, sc1, acc);
+      compute_group<CFG, OPB_T, ROW128, P2>(ops1, sc1, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -438,7 +505,7 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nblocks, int64_t ti
   tn = in / gm;
 }
 
-template <class CFG, bool OPB_T, bool ROW128>
+template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
                                                    int64_t lda, const float* __restrict__ sA,
                                                    const uint8_t* __restrict__ B, int64_t ldb,
@@ -474,7 +541,7 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
   t.K = K;
   t.g0 = split * groups_per_split;
   t.g1 = t.g0 + groups_per_split < G ? t.g0 + groups_per_split : G;
-  gemm_tile<CFG, OPB_T, ROW128>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, OPB_T, ROW128, P2>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Grouped: tiles are enumerated expert by expert, within an expert column
@@ -482,7 +549,7 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
 // workgroups share each expert's weight tile.  The per-expert row counts are
 // read from the device-resident offsets (prefix scan in LDS), so the host
 // never synchronizes; surplus workgroups of the upper-bound grid exit.
-template <class CFG, bool OPB_T>
+template <class CFG, bool OPB_T, bool P2>
 __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32_t* __restrict__ offsets,
                                                            int64_t M_total, int64_t N, int64_t K,
                                                            const uint8_t* __restrict__ A, int64_t lda,
@@ -559,7 +626,7 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   t.K = K;
   t.g0 = 0;
   t.g1 = (int)(K / 128);
-  gemm_tile<CFG, OPB_T, false>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, OPB_T, false, P2>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Split-K reduction: C[m][n] = sum over s = 0 .. S-1, in that order, of the
@@ -609,7 +676,7 @@ static size_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-template <class CFG, bool OPB_T, bool ROW128>
+template <class CFG, bool OPB_T, bool ROW128, bool P2>
 static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
                                     const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_ld, float* C,
                                     int64_t ldc, float* partials, int64_t S, hipStream_t stream) {
@@ -619,7 +686,7 @@ static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8
   const int64_t G = K / 128;
   const int64_t per = ceil_div(G, S);
   S = ceil_div(G, per);  // no empty split
-  hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128>), dim3((unsigned)blocks, (unsigned)S), dim3(CFG::NT), 0, stream, M, N,
+  hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2>), dim3((unsigned)blocks, (unsigned)S), dim3(CFG::NT), 0, stream, M, N,
                      K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per);
   if (S > 1) {
     if (hipGetLastError() != hipSuccess) return FP8BLK_ERR_LAUNCH;
@@ -631,12 +698,16 @@ static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8
 }
 
 template <class CFG, bool ROW128>
-static fp8blk_status_t dispatch_dense(bool t, int64_t M, int64_t N, int64_t K, const uint8_t* A,
+static fp8blk_status_t dispatch_dense(bool t, bool p2, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                                       int64_t lda, const float* sA, const uint8_t* B, int64_t ldb, const float* sB,
                                       int64_t sB_ld, float* C, int64_t ldc, float* partials, int64_t S,
                                       hipStream_t st) {
-  if (t) return launch_dense<CFG, true, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
-  return launch_dense<CFG, false, ROW128>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+  if (p2) {
+    if (t) return launch_dense<CFG, true, ROW128, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+    return launch_dense<CFG, false, ROW128, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+  }
+  if (t) return launch_dense<CFG, true, ROW128, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+  return launch_dense<CFG, false, ROW128, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
 }
 
 }  // namespace fp8blk
@@ -658,6 +729,8 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
                                                        const float* sB, int bscale_mode, float* C, int64_t ldc,
                                                        void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0) return FP8BLK_ERR_INVALID_ARG;
+  const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
+  opB &= ~FP8BLK_GEMM_POW2_SCALES;
   if (opB != FP8BLK_OP_N && opB != FP8BLK_OP_T) return FP8BLK_ERR_INVALID_ARG;
   if (bscale_mode != FP8BLK_BSCALE_BLOCK128 && bscale_mode != FP8BLK_BSCALE_ROW128) return FP8BLK_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP8BLK_ERR_INVALID_ARG;
@@ -694,13 +767,13 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
   if (bscale_mode == FP8BLK_BSCALE_ROW128) {
     const int64_t row_tiles = ceil_div(M, RowCfg::BM) * ceil_div(N, RowCfg::BN);
     if (row_tiles >= 128)
-      return dispatch_dense<RowCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
-    return dispatch_dense<SmallCfg, true>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+      return dispatch_dense<RowCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+    return dispatch_dense<SmallCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
   }
   const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
   if (big_tiles >= 128)
-    return dispatch_dense<BigCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
-  return dispatch_dense<SmallCfg, false>(t, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+    return dispatch_dense<BigCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+  return dispatch_dense<SmallCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
 }
 
 extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
@@ -712,6 +785,8 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   (void)workspace_bytes;
   using CFG = BigCfg;
   if (G < 0 || M_total < 0 || N < 0 || K < 0 || max_group_rows < 0) return FP8BLK_ERR_INVALID_ARG;
+  const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
+  opB &= ~FP8BLK_GEMM_POW2_SCALES;
   if (opB != FP8BLK_OP_N && opB != FP8BLK_OP_T) return FP8BLK_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP8BLK_ERR_INVALID_ARG;
   if (G == 0 || M_total == 0 || N == 0) return FP8BLK_OK;
@@ -737,12 +812,14 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   if (blocks % 8) blocks += 8 - blocks % 8;  // keep the XCD remap a bijection on the grid
   if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
   hipStream_t st = as_stream(stream);
+#define FP8BLK_GROUPED_LAUNCH(T_, P2_)                                                                         \
+  hipLaunchKernelGGL((k_grouped_gemm<CFG, T_, P2_>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G, group_offsets, \
+                     M_total, N, K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n)
   if (opB == FP8BLK_OP_T) {
-    hipLaunchKernelGGL((k_grouped_gemm<CFG, true>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G, group_offsets, M_total, N,
-                       K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n);
+    if (p2) FP8BLK_GROUPED_LAUNCH(true, true); else FP8BLK_GROUPED_LAUNCH(true, false);
   } else {
-    hipLaunchKernelGGL((k_grouped_gemm<CFG, false>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G, group_offsets, M_total, N,
-                       K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n);
+    if (p2) FP8BLK_GROUPED_LAUNCH(false, true); else FP8BLK_GROUPED_LAUNCH(false, false);
   }
+#undef FP8BLK_GROUPED_LAUNCH
   return launch_status();
 }

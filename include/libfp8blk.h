@@ -71,6 +71,16 @@ typedef enum {
 enum { FP8BLK_OP_N = 0, /* B stored [K][N] (row pitch ldb >= N)            */
        FP8BLK_OP_T = 1  /* B stored [N][K] (row pitch ldb >= K)            */ };
 
+/* Flag OR'ed into `opB` of either GEMM: every scale of A and B is a power of
+ * two in [2^-126, 2^127] (as written by the quantizers with
+ * FP8BLK_SCALE_POW2, which the pages use for some activations [p2¶4]).  The
+ * matrix cores then apply the scales themselves as E8M0 block scales and add
+ * each group's scaled product to the FP32 accumulator (round to nearest
+ * even), so no separate promotion step is needed.  A scale that is not such
+ * a power of two is read as 2^(its biased exponent - 127): the result is
+ * then wrong, not an error. */
+#define FP8BLK_GEMM_POW2_SCALES 0x100
+
 /* B scale layouts */
 enum { FP8BLK_BSCALE_BLOCK128 = 0, /* one scale per 128x128 block of B as stored:
                                       [K/128][ceil(N/128)] for OP_N,

@@ -216,3 +216,75 @@ def test_empty_is_noop():
     C = fb.gemm_fp8_blockscaled(A, torch.empty(2, 0, device="cuda"), B, torch.ones(2, 1, device="cuda"))
     torch.cuda.synchronize()
     assert C.shape == (0, 128)
+
+
+def _pow2_operands(M, N, K, opB, mode, seed):
+    """Both operands quantized with power-of-two scales, in the layouts the
+    four GEMM modes take."""
+    g = torch.Generator().manual_seed(seed)
+    A = synthetic.randn_bf16((M, K), 1.0, g)
+    qA, sA = oracle.quantize_1x128(bf16_bits(A), True)
+    if opB == oracle.OP_N:
+        B = synthetic.randn_bf16((K, N), 0.02, g)
+        if mode == oracle.BSCALE_BLOCK128:
+            qB, sB = oracle.quantize_block128(bf16_bits(B), True)
+        else:
+            qBT, sB = oracle.quantize_128x1(bf16_bits(B), True)
+            qB = np.ascontiguousarray(qBT.T)
+    else:
+        B = synthetic.randn_bf16((N, K), 0.02, g)
+        qB, sB = (oracle.quantize_block128(bf16_bits(B), True) if mode == oracle.BSCALE_BLOCK128 else
+                  oracle.quantize_1x128(bf16_bits(B), True))
+    return qA, sA, qB, sB
+
+
+@pytest.mark.parametrize("opB,mode", CASES)
+@pytest.mark.parametrize("M,N,K", [(300, 200, 384), (520, 384, 640), (256, 256, 2048)])
+def test_pow2_scales_in_matrix_cores(M, N, K, opB, mode):
+    """GEMM_POW2_SCALES: scales applied as E8M0 block scales by the MFMA and
+    groups accumulated in its FP32 accumulator.  Same gate against the
+    oracle; within FP32 rounding of the separate-fold path."""
+    qA, sA, qB, sB = _pow2_operands(M, N, K, opB, mode, M * 7 + K)
+    dev = [u8_dev(qA), f32_dev(sA), u8_dev(qB), f32_dev(sB)]
+    print(f"[gemm] pow2 scales in MFMA {M}x{N}x{K} opB={opB} mode={mode}", flush=True)
+    Cp = np_f32(fb.gemm_fp8_blockscaled(*dev, opB=opB, bscale_mode=mode, pow2_scales=True))
+    Cf = np_f32(fb.gemm_fp8_blockscaled(*dev, opB=opB, bscale_mode=mode))
+    torch.cuda.synchronize()
+    R = oracle.gemm_blockscaled(qA, sA, qB, sB, opB, mode)
+    assert e_norm(Cp, R) <= 1e-3
+    assert float(np.max(np.abs(Cp.astype(np.float64) - Cf)) / np.max(np.abs(R))) <= 1e-5
+
+
+@pytest.mark.parametrize("opB,mode", CASES)
+def test_pow2_scales_exact_small_integers(opB, mode):
+    """Small-integer codes with power-of-two scales: every product and sum is
+    exact, so the matrix-core scaling must reproduce the oracle exactly."""
+    rng = np.random.default_rng(21)
+    M, N, K = 256, 384, 512
+    G = K // 128
+    qA = _small_int_codes(rng, (M, K))
+    qB = _small_int_codes(rng, (K, N) if opB == oracle.OP_N else (N, K))
+    sA = np.exp2(rng.integers(-3, 4, size=(G, M))).astype(np.float32)
+    if mode == oracle.BSCALE_ROW128:
+        sB = np.exp2(rng.integers(-3, 4, size=(G, N))).astype(np.float32)
+    else:
+        shape = (G, 3) if opB == oracle.OP_N else (3, G)
+        sB = np.exp2(rng.integers(-3, 4, size=shape)).astype(np.float32)
+    C = np_f32(fb.gemm_fp8_blockscaled(u8_dev(qA), f32_dev(sA), u8_dev(qB), f32_dev(sB), opB=opB, bscale_mode=mode,
+                                       pow2_scales=True))
+    torch.cuda.synchronize()
+    R = oracle.gemm_blockscaled(qA, sA, qB, sB, opB, mode)
+    assert np.array_equal(C.astype(np.float64), R)
+
+
+def test_pow2_scales_dense_fprop_full_size_sampled():
+    A, W = synthetic.dense_fprop()
+    qA, sA = oracle.quantize_1x128(bf16_bits(A), True)
+    qB, sB = oracle.quantize_block128(bf16_bits(W), True)
+    print("[gemm] dense fprop 4096x4096x7168, power-of-two scales in the MFMA", flush=True)
+    C = np_f32(fb.gemm_fp8_blockscaled(u8_dev(qA), f32_dev(sA), u8_dev(qB), f32_dev(sB), pow2_scales=True))
+    torch.cuda.synchronize()
+    en = _sampled(C, qA, sA, qB, sB, oracle.OP_N, oracle.BSCALE_BLOCK128)
+    print(f"[gemm] sampled E_norm={en:.3e}", flush=True)
+    assert en <= 1e-3
+    assert np.all(np.isfinite(C))

@@ -93,3 +93,28 @@ def test_moe_up_projection_sampled():
         worst = max(worst, float(np.max(np.abs(got - Rv)) / np.max(np.abs(Rv))))
     print(f"[grouped] sampled E_norm={worst:.3e}", flush=True)
     assert worst <= 1e-3
+
+
+@pytest.mark.parametrize("opB", [oracle.OP_N, oracle.OP_T])
+def test_grouped_pow2_scales(opB):
+    """Power-of-two scales applied in the matrix cores, per expert."""
+    counts = [3, 0, 130, 257, 64]
+    print(f"[grouped] pow2 scales counts={counts} opB={opB}", flush=True)
+    K, N = 384, 256
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    Mt = int(off[-1])
+    g = torch.Generator().manual_seed(33)
+    qA, sA = oracle.quantize_1x128(bf16_bits(synthetic.randn_bf16((Mt, K), 1.0, g)), True)
+    Bs, sBs = [], []
+    for e in range(len(counts)):
+        Bshape = (K, N) if opB == oracle.OP_N else (N, K)
+        qB, sB = oracle.quantize_block128(bf16_bits(synthetic.randn_bf16(Bshape, 0.02, g)), True)
+        Bs.append(qB)
+        sBs.append(sB)
+    B, sB = np.stack(Bs), np.stack(sBs)
+    offs = torch.from_numpy(off.astype(np.int32)).cuda()
+    C = fb.grouped_gemm_fp8_blockscaled(offs, u8_dev(qA), f32_dev(sA), u8_dev(B), f32_dev(sB), opB=opB,
+                                        pow2_scales=True)
+    torch.cuda.synchronize()
+    R = oracle.grouped_gemm_blockscaled(off, qA, sA, B, sB, opB)
+    assert e_norm(np_f32(C), R) <= 1e-3
