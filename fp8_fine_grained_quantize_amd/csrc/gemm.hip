@@ -469,7 +469,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
       const int64_t col = t.n0 + wn * CFG::WTN + 16 * j + 4 * lq;
       float* dst = t.C + row * t.ldc + col;
       if (col + 3 < t.N) {
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        // streaming store: C is not read again by this kernel
+        __builtin_nontemporal_store(acc[i][j], reinterpret_cast<v4f*>(dst));
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
