@@ -179,7 +179,37 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        extras = run_extras(torch, fb, synthetic, dev, np)
+        # The same step with power-of-two scales (the pages' variant for some
+        # activations): both quantizers in pow2 mode and the GEMM applying
+        # the scales inside the matrix cores.
+        ev2 = {"step": [], "gemm": []}
+        def step_p2(i, record=False):
+            j = i % S
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record else None
+            if record:
+                e[0].record()
+            fb.quantize_1x128(A[j], pow2=True, q=qA[j], s=sA[j])
+            fb.quantize_block128(W[j], pow2=True, q=qW[j], s=sW[j])
+            if record:
+                e[1].record()
+            fb.gemm_fp8_blockscaled(qA[j], sA[j], qW[j], sW[j], C=C[j], pow2_scales=True)
+            if record:
+                e[2].record()
+                ev2["step"].append((e[0], e[2]))
+                ev2["gemm"].append((e[1], e[2]))
+        for i in range(args.warmup):
+            step_p2(i)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step_p2(i, record=True)
+        torch.cuda.synchronize()
+        t_s2 = sum(a.elapsed_time(b) for a, b in ev2["step"]) / len(ev2["step"])
+        t_g2 = sum(a.elapsed_time(b) for a, b in ev2["gemm"]) / len(ev2["gemm"])
+        extras["fprop_step_pow2_scales"] = {"ms_per_step": round(t_s2, 5), "TFLOP/s": round(flops / t_s2 / 1e9, 1),
+                                            "gemm_us": round(t_g2 * 1e3, 2),
+                                            "gemm_TFLOP/s": round(flops / t_g2 / 1e9, 1),
+                                            "gemm_frac_mfma": round(flops / t_g2 / 1e9 / FP8_PEAK_TFLOPS, 4)}
+        extras.update(run_extras(torch, fb, synthetic, dev, np))
 
     cpu = None
     if not args.no_cpu:
@@ -232,6 +262,18 @@ def run_extras(torch, fb, synthetic, dev, np):
     t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qXT, sXT, qdYT, sdYT, opB=fb.OP_T,
                                                               bscale_mode=fb.BSCALE_ROW128, C=Cw), reps)
     res["wgrad_7168x2048x4096"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(fl / t / 1e9, 1)}
+    # the same two GEMMs with power-of-two scales applied by the matrix cores
+    p_dY, p_sdY = fb.quantize_1x128(dYd, pow2=True)
+    p_W, p_sW = fb.quantize_block128(Wd, pow2=True)
+    p_XT, p_sXT = fb.quantize_128x1(Xd, pow2=True)
+    p_dYT, p_sdYT = fb.quantize_128x1(dYd, pow2=True)
+    t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(p_dY, p_sdY, p_W, p_sW, opB=fb.OP_T, C=Cd,
+                                                              pow2_scales=True), reps)
+    res["dgrad_4096x7168x2048_pow2_scales"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(fl / t / 1e9, 1)}
+    t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(p_XT, p_sXT, p_dYT, p_sdYT, opB=fb.OP_T,
+                                                              bscale_mode=fb.BSCALE_ROW128, C=Cw, pow2_scales=True), reps)
+    res["wgrad_7168x2048x4096_pow2_scales"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(fl / t / 1e9, 1)}
+    del p_dY, p_W, p_XT, p_dYT
     for name, x, fn, bpe in [("quantize_128x1_X", Xd, fb.quantize_128x1, QUANT_BYTES_1X128),
                              ("quantize_128x1_dY", dYd, fb.quantize_128x1, QUANT_BYTES_1X128),
                              ("quantize_1x128_dY", dYd, fb.quantize_1x128, QUANT_BYTES_1X128)]:
