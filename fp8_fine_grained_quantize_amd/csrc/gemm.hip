@@ -91,7 +91,7 @@ using RowCfg = TileCfg<FP8BLK_ROW_CFG>;
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
 }
 
 // --- LDS addressing -------------------------------------------------------
@@ -120,16 +120,33 @@ __device__ __forceinline__ int nmaj_off(int k, int m16) {
 // only feed output rows/columns that are never stored (column n of C depends
 // only on column n of B, row m only on row m of A), as do the padding
 // columns of a [K][N] B tile that runs past N.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
+typedef int v4i __attribute__((ext_vector_type(4)));
+// Raw buffer resource (stride 0): base address, record count, and the gfx9
+// raw-buffer flags word.
+__device__ __forceinline__ v4i rsrc_of(const void* base, int64_t bytes) {
   const int32_t n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int32_t)bytes);
-  // raw buffer (stride 0); 0x00020000 = gfx9 raw-buffer descriptor word 3
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), n, 0x00020000};
 }
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int32_t soff, uint8_t* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voff, 0, 0, 0);
+// The copies are issued from inline assembly: the compiler then does not
+// track them as pending LDS writes (its alias tracking of LDS DMA loses the
+// stage arrays apart and stalls LDS reads of the other stage on them); the K
+// loop synchronizes them itself (vmcnt wait, then barrier, before a stage is
+// read).  The instructions have no register results.
+__device__ __forceinline__ void dma16(v4i r, uint32_t voff, int32_t soff, uint8_t* lds_base) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(v4i r, uint32_t voff, uint8_t* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds_addr(lds_base))
+               : "memory", "m0");
 }
 
 // Arguments of one output tile: where its operands start and how far they
@@ -205,7 +222,7 @@ struct CopyPlan {
 
   // Resources of group g's copies.
   struct Rsrc {
-    __amdgpu_buffer_rsrc_t a, b, sa, sb;
+    v4i a, b, sa, sb;
   };
   __device__ __forceinline__ Rsrc rsrc(const TileArgs& t, int g) const {
     const int64_t k0 = (int64_t)g * 128;
@@ -231,8 +248,8 @@ struct CopyPlan {
   // Copy number n (0 .. LOADS-1) of a group: A blocks, then B blocks, then
   // the scale block.
   static constexpr int LOADS = CFG::A_ITERS + CFG::B_ITERS + 1;
-  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                            __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb, int n,
+  __device__ __forceinline__ void issue_one(v4i ra, v4i rb,
+                                            v4i rsa, v4i rsb, int n,
                                             const TileArgs& t, uint8_t* buf, float* sbuf) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (n < CFG::A_ITERS) {
