@@ -12,8 +12,9 @@ so reads come from HBM.
 `value` = 2*M*N*K / step time (TFLOP/s of the whole step, quantizers
 included).  `roofline` reports the GEMM kernel alone (average duration from
 HIP events around each launch in the timed region) against the dense FP8
-MFMA peak.  `kernels` adds each kernel's time and roofline fraction (events
-between the step's kernels), and `extras` times the other workloads' kernels
+MFMA peak.  `kernels` adds each kernel's time and roofline fraction (the
+quantizers from a second pass of the same steps with events between all
+kernels), and `extras` times the other workloads' kernels
 (backward Dgrad/Wgrad, the accumulation study, the MoE grouped GEMMs).
 `cpu_baseline` times the CPU oracle on a bounded sample of the step.
 
@@ -48,8 +49,10 @@ GEMM_TRAFFIC = {"sha256": "a9322ece6b366272c10857cac3b17d8464bd29bb484cbd7e037bc
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps; the warm-up also runs for at least --warmup-seconds")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0)
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -70,6 +73,60 @@ def calibrate_copy(torch):
                       "bytes_written_per_launch": 1 << 30, "us": round(t * 1e3, 2), "GB/s": round(gbs, 1)}))
 
 
+class HipEvents:
+    """Timing events recorded on the current HIP stream without the
+    system-scope fence that torch's events carry (timestamps only, no cache
+    write-back to host scope, which costs each record several microseconds
+    of GPU time)."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, torch):
+        import ctypes
+        self.ct = ctypes
+        self.torch = torch
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def record(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.pool.append(e)
+        if self.hip.hipEventRecord(e, self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        return e
+
+    def ms(self, a, b):
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def release(self):
+        for e in self.pool:
+            self.hip.hipEventDestroy(e)
+        self.pool = []
+
+
+def warm_up(torch, fn, min_seconds):
+    """Run fn(i) until at least min_seconds of GPU work have passed: the GPU
+    raises its clocks only after tens of milliseconds under load."""
+    i = 0
+    t0 = time.perf_counter()
+    while True:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= min_seconds:
+                return i
+
+
 def gemm_traffic():
     """Measured HBM bytes per GEMM launch if the GEMM source is unchanged."""
     import hashlib
@@ -81,21 +138,24 @@ def gemm_traffic():
 
 
 def timed_events(torch, fn, reps):
-    """Average duration (ms) of fn() over reps launches, HIP events on the
-    current stream around each launch.  A sleep kernel queued first keeps the
-    GPU busy while the host enqueues the launches, so that each event pair
-    brackets GPU work only (short kernels would otherwise wait on the host)."""
+    """Average duration (ms) of fn() over reps launches, HIP events (no
+    system fence) on the current stream around each launch.  A sleep kernel
+    queued first keeps the GPU busy while the host enqueues the launches, so
+    that each event pair brackets GPU work only (short kernels would
+    otherwise wait on the host)."""
     fn(0)
     torch.cuda.synchronize()
+    hev = HipEvents(torch)
     torch.cuda._sleep(4_000_000)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    pairs = []
     for i in range(reps):
-        starts[i].record()
+        a = hev.record()
         fn(i)
-        ends[i].record()
+        pairs.append((a, hev.record()))
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
+    t = sum(hev.ms(a, b) for a, b in pairs) / reps
+    hev.release()
+    return t
 
 
 def main():
@@ -126,47 +186,54 @@ def main():
     sW = [torch.empty(K // 128, N // 128, dtype=torch.float32, device=dev) for _ in range(S)]
     C = [torch.empty(M, N, dtype=torch.float32, device=dev) for _ in range(S)]
 
+    # Events around the GEMM only: each event record costs the step several
+    # microseconds of GPU time, so the quantizers are timed in a second pass.
     ev = {k: [] for k in ("q1x128", "qblock", "gemm")}
 
-    def step(i, record=False):
+    hev = HipEvents(torch)
+
+    def step(i, record=False, per_kernel=False):
         j = i % S
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
-        if record:
-            e[0].record()
+        e0 = hev.record() if per_kernel else None
         fb.quantize_1x128(A[j], q=qA[j], s=sA[j])
-        if record:
-            e[1].record()
+        e1 = hev.record() if per_kernel else None
         fb.quantize_block128(W[j], q=qW[j], s=sW[j])
-        if record:
-            e[2].record()
+        e2 = hev.record() if record else None
         fb.gemm_fp8_blockscaled(qA[j], sA[j], qW[j], sW[j], opB=fb.OP_N, bscale_mode=fb.BSCALE_BLOCK128, C=C[j])
         if record:
-            e[3].record()
-            ev["q1x128"].append((e[0], e[1]))
-            ev["qblock"].append((e[1], e[2]))
-            ev["gemm"].append((e[2], e[3]))
+            e3 = hev.record()
+            ev["gemm"].append((e2, e3))
+            if per_kernel:
+                ev["q1x128"].append((e0, e1))
+                ev["qblock"].append((e1, e2))
 
     for i in range(args.warmup):
         step(i)
+    warm_up(torch, step, args.warmup_seconds)
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps, synchronized on both sides.
     t0 = time.perf_counter()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    start = hev.record()
     for i in range(args.steps):
         step(i, record=True)
-    end.record()
+    end = hev.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = hev.ms(start, end) / args.steps
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
 
     def avg(k):
-        return sum(a.elapsed_time(b) for a, b in ev[k]) / len(ev[k])
+        return sum(hev.ms(a, b) for a, b in ev[k]) / len(ev[k])
 
-    t_q1, t_qb, t_g = avg("q1x128"), avg("qblock"), avg("gemm")
+    t_g = avg("gemm")
+    # Second pass, outside the timed region: the same steps with events
+    # between all three kernels, for the quantizers' durations.
+    for i in range(args.steps):
+        step(i, record=True, per_kernel=True)
+    torch.cuda.synchronize()
+    t_q1, t_qb = avg("q1x128"), avg("qblock")
     gemm_tflops = flops / (t_g * 1e-3) / 1e12
     q1_gbs = M * K * QUANT_BYTES_1X128 / (t_q1 * 1e-3) / 1e9
     qb_gbs = K * N * QUANT_BYTES_BLOCK / (t_qb * 1e-3) / 1e9
@@ -182,29 +249,25 @@ def main():
         # The same step with power-of-two scales (the pages' variant for some
         # activations): both quantizers in pow2 mode and the GEMM applying
         # the scales inside the matrix cores.
-        ev2 = {"step": [], "gemm": []}
+        ev2 = {"gemm": []}
         def step_p2(i, record=False):
             j = i % S
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record else None
-            if record:
-                e[0].record()
             fb.quantize_1x128(A[j], pow2=True, q=qA[j], s=sA[j])
             fb.quantize_block128(W[j], pow2=True, q=qW[j], s=sW[j])
-            if record:
-                e[1].record()
+            e0 = hev.record() if record else None
             fb.gemm_fp8_blockscaled(qA[j], sA[j], qW[j], sW[j], C=C[j], pow2_scales=True)
             if record:
-                e[2].record()
-                ev2["step"].append((e[0], e[2]))
-                ev2["gemm"].append((e[1], e[2]))
+                ev2["gemm"].append((e0, hev.record()))
         for i in range(args.warmup):
             step_p2(i)
         torch.cuda.synchronize()
+        s0 = hev.record()
         for i in range(args.steps):
             step_p2(i, record=True)
+        s1 = hev.record()
         torch.cuda.synchronize()
-        t_s2 = sum(a.elapsed_time(b) for a, b in ev2["step"]) / len(ev2["step"])
-        t_g2 = sum(a.elapsed_time(b) for a, b in ev2["gemm"]) / len(ev2["gemm"])
+        t_s2 = hev.ms(s0, s1) / args.steps
+        t_g2 = sum(hev.ms(a, b) for a, b in ev2["gemm"]) / len(ev2["gemm"])
         extras["fprop_step_pow2_scales"] = {"ms_per_step": round(t_s2, 5), "TFLOP/s": round(flops / t_s2 / 1e9, 1),
                                             "gemm_us": round(t_g2 * 1e3, 2),
                                             "gemm_TFLOP/s": round(flops / t_g2 / 1e9, 1),
@@ -239,6 +302,7 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
+    hev.release()
     print(json.dumps(out))
 
 
@@ -321,7 +385,16 @@ def run_extras(torch, fb, synthetic, dev, np):
                                                     "GB/s": round(byts / t / 1e6, 1),
                                                     "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4),
                                                     "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
-    del qU, sU
+    # The up projection with power-of-two weight scales too (its input is the
+    # pages' power-of-two activation), the scales then applied by the MFMA.
+    Cu2 = torch.empty(Mt, Nu, dtype=torch.float32, device=dev)
+    for e in range(G):
+        fb.quantize_block128(synthetic.expert_weight("up", e, device=dev), pow2=True, q=qU[e], s=sU[e])
+    t = timed_events(torch, lambda i: fb.grouped_gemm_fp8_blockscaled(offs, qA, sA, qU, sU, C=Cu2, pow2_scales=True), 3)
+    res["grouped_up_gate_65536x4096x7168_E256_pow2_scales"] = {"us": round(t * 1e3, 1),
+                                                               "TFLOP/s": round(fl / t / 1e9, 1),
+                                                               "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4)}
+    del qU, sU, Cu2
     torch.cuda.empty_cache()
     H = (torch.nn.functional.silu(Cu[:, :2048]) * Cu[:, 2048:]).to(torch.bfloat16)
     del Cu
