@@ -307,11 +307,7 @@ template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
                                               v4f (&acc)[CFG::TM][CFG::TN]) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
-  // The LDS addresses below are recomputed for every K group from an
-  // opaque copy of the thread index: held across the loop for both stages
-  // they would not fit in the register budget.
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
