@@ -95,15 +95,32 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // --- LDS addressing -------------------------------------------------------
+// Both swizzles were picked by measuring the LDS read rate of the exact
+// fragment read patterns on gfx950 (one CU, eight waves, reads back to back):
+// a swizzle that looks conflict-free for 16-lane phases can still run at
+// half rate there.
+//
 // K-major tile [rows][128 bytes]: 16-byte chunk c of row r lives at chunk
-// c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int kmaj_off(int r, int c16) { return r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4); }
+// c ^ kmaj_swz(r).  A fragment read has lane l take row 16*i + l%16, chunk
+// 2*(l/16) (+1).  Measured: 4.0 cycles per 1 KB ds_read_b128 (the rate of a
+// linear read) with this swizzle, 8.1 with c ^ ((r >> 1) & 7) or c ^ (r & 7).
+__device__ __forceinline__ int kmaj_swz(int r) { return ((r >> 1) & 1) | (r & 4); }
+__device__ __forceinline__ int kmaj_off(int r, int c16) { return r * 128 + ((c16 ^ kmaj_swz(r)) << 4); }
 
 // N-major tile [128 k][BN bytes]: 16-byte chunk m of row k lives at chunk
-// m ^ (k & 7) (BN >= 128), keeping the two 8-byte halves of a chunk adjacent.
+// m ^ nmaj_swz(k) (BN >= 128), keeping the two 8-byte halves of a chunk
+// adjacent.  A transposing fragment read has the 16-lane group g = l/16 read
+// rows 32*g + 8*r + (0..7); bit 5 of k (g odd) moves those rows to the other
+// half of a 256-byte row (BN = 256) or to the odd chunks (BN = 128).
+// Measured: 2.6 cycles per ds_read_b64_tr_b8 (2.35 for a linear read) against
+// 4.0 with m ^ (k & 7) alone.
+template <int BN>
+__device__ __forceinline__ int nmaj_swz(int k) {
+  return (k & 7) ^ (((k >> 5) & 1) * (BN >= 256 ? 8 : 1));
+}
 template <int BN>
 __device__ __forceinline__ int nmaj_off(int k, int m16) {
-  return k * BN + ((m16 ^ (k & 7)) << 4);
+  return k * BN + ((m16 ^ nmaj_swz<BN>(k)) << 4);
 }
 
 // Direct global->LDS copies through buffer resources: buffer_load_dwordx4
@@ -176,10 +193,13 @@ template <class CFG, bool OPB_T, bool ROW128>
 struct CopyPlan {
   static constexpr int NW = CFG::NW, BM = CFG::BM, BN = CFG::BN;
   // [K][N] B tile: BN/16 chunks per k row, so one copy iteration advances k
-  // by KSTEP rows; the row swizzle (k & 7) must repeat across iterations.
+  // by KSTEP rows: k = it * KSTEP + (the lane's row).  Then k & 7 is the same
+  // in every iteration, and bit 5 of k is the lane's own (KSTEP a multiple of
+  // 64) or flips on odd iterations (KSTEP = 32 mod 64): two per-lane offsets
+  // cover both.
   static constexpr int KSTEP = NW * 64 / (BN / 16);
-  static_assert(KSTEP % 8 == 0, "[K][N] copies keep the row swizzle across iterations");
-  uint32_t a, b, sc;
+  static_assert(KSTEP % 32 == 0, "[K][N] copies: bit 5 of k per lane or alternating per iteration");
+  uint32_t a, b, b2, sc;
 
   __device__ __forceinline__ void init(const TileArgs& t) {
     constexpr int TM = CFG::TM, WTM = CFG::WTM;
@@ -187,15 +207,18 @@ struct CopyPlan {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     {  // A and [N][K] B: chunk ci = (it*NW + wave)*64 + lane; row ci/8 advances by 8*NW per it
       const int ci = wave * 64 + lane;
-      const int r = ci >> 3, c = (ci & 7) ^ ((r >> 1) & 7);
+      const int r = ci >> 3, c = (ci & 7) ^ kmaj_swz(r);
       a = (uint32_t)(r * t.lda + c * 16);
-      if (OPB_T) b = (uint32_t)(r * t.ldb + c * 16);
+      if (OPB_T) b = b2 = (uint32_t)(r * t.ldb + c * 16);
     }
     if (!OPB_T) {  // [K][N] B: BN/16 chunks per k row; k advances by KSTEP per it
       constexpr int CPR = BN / 16;
       const int ci = wave * 64 + lane;
-      const int k = ci / CPR, m = (ci % CPR) ^ (k & 7);
-      b = (uint32_t)(k * t.ldb + m * 16);
+      const int k = ci / CPR, p16 = ci % CPR;
+      // global chunk for LDS position p16 when bit 5 of k is that of this
+      // lane's row (b) or its complement (b2, the odd iterations)
+      b = (uint32_t)(k * t.ldb + (p16 ^ nmaj_swz<BN>(k)) * 16);
+      b2 = KSTEP % 64 == 0 ? b : (uint32_t)(k * t.ldb + (p16 ^ nmaj_swz<BN>(k ^ 32)) * 16);
     }
     int blk = wave;
     if (blk >= CFG::S_BLOCKS) blk = 0;  // surplus copy: rewrites block 0 with the same data
@@ -258,16 +281,24 @@ struct CopyPlan {
     } else if (n < CFG::A_ITERS + CFG::B_ITERS) {
       const int it = n - CFG::A_ITERS;
       const int32_t so = OPB_T ? (int32_t)(it * 8 * NW * t.ldb) : (int32_t)(it * KSTEP * t.ldb);
-      dma16(rb, b, so, buf + CFG::A_BYTES + (it * NW + wave) * 1024);
+      dma16(rb, (!OPB_T && (it & 1)) ? b2 : b, so, buf + CFG::A_BYTES + (it * NW + wave) * 1024);
     } else {
       const int blk = wave < CFG::S_BLOCKS ? wave : 0;
-      if (blk * 64 < BM)
-        dma4(rsa, sc, (uint8_t*)(sbuf + blk * 64));
-      else
-        dma4(rsb, sc, (uint8_t*)(sbuf + blk * 64));
+      const bool rows = blk * 64 < BM;  // wave-uniform; a select keeps the copy branch-free
+      const v4i rs = v4i{rows ? rsa[0] : rsb[0], rows ? rsa[1] : rsb[1], rows ? rsa[2] : rsb[2], rows ? rsa[3] : rsb[3]};
+      dma4(rs, sc, (uint8_t*)(sbuf + blk * 64));
     }
   }
 };
+
+// Whether a kernel issues the next group's copies from inside its row loop
+// (the power-of-two path of tiles with ILV_MIN_TM or more row tiles per
+// wave) instead of all at the group start.
+#ifndef FP8BLK_ILV_MIN_TM
+#define FP8BLK_ILV_MIN_TM 8
+#endif
+template <class CFG, bool P2>
+constexpr bool interleaved_copies() { return P2 && CFG::TM >= FP8BLK_ILV_MIN_TM; }
 
 // One K group of MFMAs and scale folds on operands already in LDS (`ops`:
 // A tile then B tile; `sc`: row scales in lane order, then column/block
@@ -305,7 +336,9 @@ __device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s
 
 template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
-                                              v4f (&acc)[CFG::TM][CFG::TN]) {
+                                              v4f (&acc)[CFG::TM][CFG::TN],
+                                              const CopyPlan<CFG, OPB_T, ROW128>& plan, const TileArgs& t, int gnext,
+                                              uint8_t* nbuf, float* nsbuf) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -382,14 +415,36 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
     } else {
       sbe = e8m0_of(sbb);
     }
-    v8i afr = load_a(0);
+    // The copies of group gnext are spread over the row tiles (issued all at
+    // the group start they hold up the first MFMAs); with no next group
+    // (gnext < 0) the resources get a zero record count, so the same
+    // instructions read nothing and the loop has no branch.  A fragments are
+    // read two row tiles ahead, and a scheduling fence after each row tile
+    // keeps the next reads and copies from being hoisted above its MFMAs.
+    using Plan = CopyPlan<CFG, OPB_T, ROW128>;
+    constexpr int LOADS = Plan::LOADS;
+    constexpr bool ILV = interleaved_copies<CFG, P2>();
+    typename Plan::Rsrc cr;
+    if constexpr (ILV) {
+      cr = plan.rsrc(t, gnext >= 0 ? gnext : t.g0);
+      const int on = gnext >= 0 ? -1 : 0;
+      cr.a[2] &= on; cr.b[2] &= on; cr.sa[2] &= on; cr.sb[2] &= on;
+    }
+    v8i af[TM];
+    af[0] = load_a(0);
+    if (TM > 1) af[1] = load_a(1);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
+      if (i + 2 < TM) af[i + 2] = load_a(i + 2);
+      if constexpr (ILV) {
+#pragma unroll
+        for (int n = (i * LOADS) / TM; n < ((i + 1) * LOADS) / TM; ++n)
+          plan.issue_one(cr.a, cr.b, cr.sa, cr.sb, n, t, nbuf, nsbuf);
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = mfma_e8m0_sel(ROW128 ? j : 0, i % 4, bfr[j], afr, acc[i][j], sbe, sae[i / 4]);
-      afr = anext;
+        acc[i][j] = mfma_e8m0_sel(ROW128 ? j : 0, i % 4, bfr[j], af[i], acc[i][j], sbe, sae[i / 4]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     return;
   }
@@ -442,6 +497,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
   const int l16 = lane & 15, lq = lane >> 4;
   const int g0 = t.g0, G = t.g1;
 
+  constexpr bool ILV = interleaved_copies<CFG, P2>();
   CopyPlan<CFG, OPB_T, ROW128> plan;
   plan.init(t);
 
@@ -455,22 +511,25 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
   for (int g = g0; g < G; g += 2) {
     // Group g has landed in stage 0 once this lane's copies are complete;
     // after the barrier every wave's copies are visible and every wave is
-    // done reading stage 1 (group g-1), which then receives group g+1.
+    // done reading stage 1 (group g-1), which then receives group g+1 (with
+    // interleaved copies, from inside compute_group).
     wait_vmcnt<0>();
     __syncthreads();
-    if (g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
+    if (!ILV && g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_group<CFG, OPB_T, ROW128, P2>(ops0, sc0, acc);
+    compute_group<CFG, OPB_T, ROW128, P2>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
     if (g + 1 < G) {
       wait_vmcnt<0>();
       __syncthreads();
-      if (g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
+      if (!ILV && g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group<CFG, OPB_T, ROW128, P2>(ops1, sc1, acc);
+      compute_group<CFG, OPB_T, ROW128, P2>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+
+  if (ILV) wait_vmcnt<0>();  // the last group's (empty) interleaved copies
 
   // ---- epilogue: FP32 C, four consecutive columns per lane ----
 #pragma unroll
