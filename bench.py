@@ -138,8 +138,9 @@ def gemm_traffic():
 
 
 def timed_events(torch, fn, reps):
-    """Average duration (ms) of fn() over reps launches, HIP events (no
-    system fence) on the current stream around each launch.  A sleep kernel
+    """Median duration (ms) of fn() over reps launches, HIP events (no
+    system fence) on the current stream around each launch (the median keeps
+    a rare host or system hiccup out of the figure).  A sleep kernel
     queued first keeps the GPU busy while the host enqueues the launches, so
     that each event pair brackets GPU work only (short kernels would
     otherwise wait on the host)."""
@@ -153,9 +154,9 @@ def timed_events(torch, fn, reps):
         fn(i)
         pairs.append((a, hev.record()))
     torch.cuda.synchronize()
-    t = sum(hev.ms(a, b) for a, b in pairs) / reps
+    ts = sorted(hev.ms(a, b) for a, b in pairs)
     hev.release()
-    return t
+    return ts[len(ts) // 2]
 
 
 def main():
@@ -411,6 +412,45 @@ def run_extras(torch, fb, synthetic, dev, np):
                                                  "GB/s": round(byts / t / 1e6, 1),
                                                  "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4),
                                                  "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
+    del qH, sH, Cdn
+    torch.cuda.empty_cache()
+    # MoE backward of the down projection.  Dgrad: dH_e = dOut_e W_down[e]^T
+    # (the stored expert weights read transposed); Wgrad: dW_down[e] =
+    # H_e^T dOut_e with both operands quantized 128x1 along tokens inside each
+    # expert (ragged token groups).
+    dO = synthetic.moe_grad("dout", Mt, device=dev)
+    qdO, sdO = fb.quantize_1x128(dO)
+    CdH = torch.empty(Mt, 2048, dtype=torch.float32, device=dev)
+    t = timed_events(torch, lambda i: fb.grouped_gemm_fp8_blockscaled(offs, qdO, sdO, qD, sD, opB=fb.OP_T, C=CdH), 3)
+    fl = 2.0 * Mt * 2048 * Nd
+    byts = G * 2048 * Nd + Mt * Nd + Mt * 2048 * 4
+    res["grouped_dgrad_down_65536x2048x7168_E256"] = {"us": round(t * 1e3, 1), "TFLOP/s": round(fl / t / 1e9, 1),
+                                                       "GB/s": round(byts / t / 1e6, 1),
+                                                       "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4),
+                                                       "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
+    del CdH, qD, sD, qdO, sdO
+    torch.cuda.empty_cache()
+    counts = (r["offsets"][1:] - r["offsets"][:-1]).tolist()
+    groups = sum((c + 127) // 128 for c in counts)          # ragged 128-token groups over all experts
+    AT, sAT = fb.quantize_128x1_grouped(H, offs)
+    BT, sBT = fb.quantize_128x1_grouped(dO, offs)
+    for name, src, qT_, s_ in (("H", H, AT, sAT), ("dOut", dO, BT, sBT)):
+        t = timed_events(torch, lambda i: fb.quantize_128x1_grouped(src, offs, qT=qT_, s=s_), reps)
+        cols = src.shape[1]
+        byts = cols * (2 * Mt + 128 * groups) + 4 * groups * cols
+        res[f"quantize_128x1_grouped_{name}_{Mt}x{cols}_E256"] = {"us": round(t * 1e3, 2),
+                                                                  "GB/s": round(byts / t / 1e6, 1),
+                                                                  "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
+    Wd = torch.empty(G, 2048, Nd, dtype=torch.float32, device=dev)
+    t = timed_events(torch, lambda i: fb.grouped_wgrad_fp8_blockscaled(offs, Mt, AT, sAT, BT, sBT, C=Wd), 3)
+    fl = 2.0 * Mt * 2048 * Nd
+    byts = G * 2048 * Nd * 4 + (2048 + Nd) * 128 * groups + 4 * groups * (2048 + Nd)
+    res["grouped_wgrad_down_2048x7168_T65536_E256"] = {"us": round(t * 1e3, 1), "TFLOP/s": round(fl / t / 1e9, 1),
+                                                        "GB/s": round(byts / t / 1e6, 1),
+                                                        "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4),
+                                                        "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
+    del Wd, AT, BT, sAT, sBT, dO, H
+    torch.cuda.empty_cache()
     return res
 
 

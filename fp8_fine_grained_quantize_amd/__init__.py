@@ -20,6 +20,7 @@ __all__ = [
     "Fp8BlkError", "lib", "library_path", "OP_N", "OP_T", "BSCALE_BLOCK128", "BSCALE_ROW128",
     "SCALE_POW2", "GEMM_POW2_SCALES", "quantize_1x128", "quantize_128x1", "quantize_block128",
     "requantize_128x1_from_1x128", "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled",
+    "quantize_128x1_grouped", "token_group_slots", "grouped_wgrad_fp8_blockscaled",
     "workspace_bytes", "status_string", "abi_version", "EXPORTED_SYMBOLS", "empty_pitched", "as_pitched",
 ]
 
@@ -41,6 +42,10 @@ _SIGNATURES = {
                                            _vp, _i64, _vp, _sz, _vp]),
     "fp8blk_grouped_gemm_fp8_blockscaled": (_int, [_i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
                                                    _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "fp8blk_quantize_128x1_grouped": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _u32, _vp]),
+    "fp8blk_token_group_slots": (_i64, [_i64, _i64]),
+    "fp8blk_grouped_wgrad_fp8_blockscaled": (_int, [_i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64,
+                                                    _vp, _u32, _vp, _i64, _i64, _vp]),
     "fp8blk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "fp8blk_status_string": (ctypes.c_char_p, [_int]),
     "fp8blk_abi_version": (_int, []),
@@ -230,4 +235,44 @@ def grouped_gemm_fp8_blockscaled(offsets, A, sA, B, sB, opB: int = OP_N, max_gro
         G, _ptr(offsets), M, mgr, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), B.stride(1), B.stride(0),
         opB | (GEMM_POW2_SCALES if pow2_scales else 0),
         _ptr(sB), sB.stride(0), _ptr(C), _pitch(C), None, 0, _stream()), "grouped_gemm_fp8_blockscaled")
+    return C
+
+
+def token_group_slots(T: int, G: int) -> int:
+    """Group slots to allocate for T tokens split into G experts (T//128 + G)."""
+    return lib().fp8blk_token_group_slots(T, G)
+
+
+def quantize_128x1_grouped(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = False, qT=None, s=None):
+    """MoE Wgrad operand: x [T][C] bf16 (tokens in expert order), offsets
+    device int32 [G+1] -> (qT uint8 [C][128*S], s float32 [S][C]) with
+    S = token_group_slots(T, G); expert e's token j is column 128*PG[e] + j,
+    PG[e] = sum of ceil(M_e'/128) over e' < e (see the header)."""
+    x = _bf16_bits(x)
+    T, C = x.shape
+    G = offsets.numel() - 1
+    assert offsets.dtype == torch.int32 and offsets.is_cuda
+    S = token_group_slots(T, G)
+    qT = _empty_pitched(C, 128 * S, torch.uint8, x.device, 1) if qT is None else qT
+    s = torch.empty(S, C, dtype=torch.float32, device=x.device) if s is None else s
+    _check(lib().fp8blk_quantize_128x1_grouped(_ptr(x), T, C, _pitch(x), G, _ptr(offsets), _ptr(qT), _pitch(qT),
+                                               _ptr(s), SCALE_POW2 if pow2 else 0, _stream()),
+           "quantize_128x1_grouped")
+    return qT, s
+
+
+def grouped_wgrad_fp8_blockscaled(offsets: torch.Tensor, T: int, AT, sA, BT, sB, C=None, pow2_scales: bool = False):
+    """MoE grouped Wgrad: dW_e = X_e^T dY_e for every expert from the outputs
+    of quantize_128x1_grouped of X (AT [M][128*S], sA) and of dY (BT
+    [N][128*S], sB) with the same offsets and T.  Returns C float32 [G][M][N]."""
+    G = offsets.numel() - 1
+    assert offsets.dtype == torch.int32 and offsets.is_cuda
+    M, N = AT.shape[0], BT.shape[0]
+    if C is None:
+        C = torch.empty(G, M, _pad16(N, 4), dtype=torch.float32, device=AT.device)[:, :, :N]
+    assert C.dim() == 3 and C.stride(2) == 1
+    _check(lib().fp8blk_grouped_wgrad_fp8_blockscaled(
+        G, _ptr(offsets), T, M, N, _ptr(AT), _pitch(AT), _ptr(sA), _ptr(BT), _pitch(BT), _ptr(sB),
+        GEMM_POW2_SCALES if pow2_scales else 0, _ptr(C), C.stride(1), C.stride(0), _stream()),
+        "grouped_wgrad_fp8_blockscaled")
     return C

@@ -37,6 +37,7 @@
 //   column l%16.
 #include "fp8_device.h"
 #include "host_common.h"
+#include "token_groups.h"
 
 namespace fp8blk {
 
@@ -507,7 +508,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  plan.issue(t, g0, ops0, sc0);
+  if (g0 < G) plan.issue(t, g0, ops0, sc0);  // no groups (an expert without tokens): C = 0
   for (int g = g0; g < G; g += 2) {
     // Group g has landed in stage 0 once this lane's copies are complete;
     // after the barrier every wave's copies are visible and every wave is
@@ -699,6 +700,50 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   t.g0 = 0;
   t.g1 = (int)(K / 128);
   gemm_tile<CFG, OPB_T, false, P2>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+}
+
+// Grouped Wgrad of MoE experts: dW_e = X_e^T dY_e for every expert e, both
+// operands 128x1-quantized along tokens inside each expert (ragged token
+// groups, token_groups.h) and stored transposed, so that expert e's K range
+// is its own group slots [PG[e], PG[e] + n_e) of the shared code matrices.
+// Every expert's output has the same M x N tiles; tiles are enumerated expert
+// by expert, column tile by column tile, row tiles innermost.  An expert
+// without tokens gets dW_e = 0.
+template <class CFG, bool P2>
+__global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __restrict__ offsets, int64_t M, int64_t N,
+                                                            const uint8_t* __restrict__ A, int64_t lda,
+                                                            const float* __restrict__ sA,
+                                                            const uint8_t* __restrict__ B, int64_t ldb,
+                                                            const float* __restrict__ sB, float* __restrict__ C,
+                                                            int64_t ldc, int64_t strideC, int64_t tiles_m,
+                                                            int64_t tiles_n) {
+  FP8BLK_DECLARE_STAGES(CFG);
+  __shared__ int64_t s_red[CFG::NT];
+  const int64_t per = tiles_m * tiles_n;
+  const int64_t lin = blockIdx.x;
+  const int64_t e = lin / per, rem = lin % per;
+  const int64_t tn = rem / tiles_m, tm = rem % tiles_m;
+  const int64_t pg = token_group_start<CFG::NT>(offsets, e, s_red);
+  const int64_t ng = token_groups_of(offsets, e);
+  const int64_t m0 = tm * CFG::BM;
+  TileArgs t;
+  t.A = A + m0 * lda;
+  t.lda = lda;
+  t.rows = (M - m0) < CFG::BM ? (M - m0) : CFG::BM;
+  t.sA = sA + m0;
+  t.sA_ld = M;
+  t.B = B;
+  t.ldb = ldb;
+  t.n0 = tn * CFG::BN;
+  t.N = N;
+  t.sB = sB;
+  t.sB_ld = N;
+  t.C = C + e * strideC + m0 * ldc;
+  t.ldc = ldc;
+  t.K = 128 * (pg + ng);
+  t.g0 = (int)pg;
+  t.g1 = (int)(pg + ng);
+  gemm_tile<CFG, true, true, P2>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Split-K reduction: C[m][n] = sum over s = 0 .. S-1, in that order, of the
@@ -896,5 +941,40 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
     if (p2) FP8BLK_GROUPED_LAUNCH(false, true); else FP8BLK_GROUPED_LAUNCH(false, false);
   }
 #undef FP8BLK_GROUPED_LAUNCH
+  return launch_status();
+}
+
+extern "C" fp8blk_status_t fp8blk_grouped_wgrad_fp8_blockscaled(int64_t G, const int32_t* group_offsets, int64_t T,
+                                                                int64_t M, int64_t N, const uint8_t* AT,
+                                                                int64_t ldaT, const float* sA, const uint8_t* BT,
+                                                                int64_t ldbT, const float* sB, uint32_t flags,
+                                                                float* C, int64_t ldc, int64_t strideC,
+                                                                void* stream) {
+  // 128 x 128 tiles: the per-column scales of both operands (ROW128) need the
+  // registers of the smaller tile.
+  using CFG = RowCfg;
+  if (G < 0 || T < 0 || M < 0 || N < 0) return FP8BLK_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)FP8BLK_GEMM_POW2_SCALES) return FP8BLK_ERR_INVALID_ARG;
+  const bool p2 = (flags & FP8BLK_GEMM_POW2_SCALES) != 0;
+  if (G == 0 || M == 0 || N == 0) return FP8BLK_OK;
+  const int64_t slots = fp8blk_token_group_slots(T, G);
+  if (group_offsets == nullptr || !aligned(group_offsets, 4)) return FP8BLK_ERR_INVALID_ARG;
+  if (T > 0) {  // with no tokens the operands are not read (every dW_e = 0)
+    if (!matrix_ok(AT, M, 128 * slots, ldaT, 1) || !matrix_ok(BT, N, 128 * slots, ldbT, 1))
+      return FP8BLK_ERR_INVALID_ARG;
+    if (!vec_ok(sA, slots * M) || !vec_ok(sB, slots * N)) return FP8BLK_ERR_INVALID_ARG;
+  }
+  if (!matrix_ok(C, M, N, ldc, 4) || strideC < M * ldc || strideC % 4 != 0) return FP8BLK_ERR_INVALID_ARG;
+  if (ldaT >= kMaxPitch || ldbT >= kMaxPitch || slots > 0x7FFFFFFF / 2) return FP8BLK_ERR_UNSUPPORTED;
+  const int64_t tiles_m = ceil_div(M, CFG::BM), tiles_n = ceil_div(N, CFG::BN);
+  const int64_t blocks = G * tiles_m * tiles_n;
+  if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
+  hipStream_t st = as_stream(stream);
+  if (p2)
+    hipLaunchKernelGGL((k_grouped_wgrad<CFG, true>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, group_offsets, M, N,
+                       AT, ldaT, sA, BT, ldbT, sB, C, ldc, strideC, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((k_grouped_wgrad<CFG, false>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, group_offsets, M,
+                       N, AT, ldaT, sA, BT, ldbT, sB, C, ldc, strideC, tiles_m, tiles_n);
   return launch_status();
 }

@@ -13,6 +13,7 @@
 // operations (1x128: one 128-element tile = 16 lanes x 16 bytes = one DPP row).
 #include "fp8_device.h"
 #include "host_common.h"
+#include "token_groups.h"
 
 namespace fp8blk {
 
@@ -156,6 +157,11 @@ __global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restric
 // 4 waves through LDS.  Codes go through an LDS tile laid out [channel][token]
 // so that the transposed rows of qT are written as contiguous 16-byte chunks.
 // The tile's 8-byte segments are XOR-swizzled by channel/8 to spread banks.
+// GROUPED: the tokens are split into MoE experts by device-resident offsets
+// and each expert is tiled separately (ragged 128-token groups, see
+// token_groups.h); workgroup row blockIdx.y is one group slot, a slot past
+// the last expert's groups exits, and the tokens of a partial group beyond
+// the expert's end are stored as code 0 so that the GEMM reads zeros there.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   const uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
@@ -163,17 +169,30 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return lo | (hi << 16);
 }
 
-template <bool POW2>
+template <bool POW2, bool GROUPED>
 __global__ __launch_bounds__(256) void k_quant_128x1(const uint16_t* __restrict__ x, int64_t T, int64_t C,
                                                       int64_t ldx, uint8_t* __restrict__ qT, int64_t ldqT,
-                                                      float* __restrict__ s) {
+                                                      float* __restrict__ s, const int32_t* __restrict__ off,
+                                                      int64_t G) {
   __shared__ uint32_t red[4][16][4];
   __shared__ float sh_s[128], sh_r[128];
   __shared__ int sh_slow[128];
   __shared__ __align__(16) uint8_t tile[128 * 128];
 
   const int64_t c0 = (int64_t)blockIdx.x * 128;
-  const int64_t t0 = (int64_t)blockIdx.y * 128;
+  // Input tokens [t0, t_end) of this tile (at most 128), stored at columns
+  // [o0, o_end) of qT.
+  int64_t t0 = (int64_t)blockIdx.y * 128, t_end = T;
+  int64_t o0 = t0, o_end = T;
+  if (GROUPED) {
+    __shared__ int64_t sh_scan[257], sh_found[2];
+    int64_t e, local;
+    token_group_owner<256>(off, G, blockIdx.y, sh_scan, sh_found, e, local);
+    if (e < 0) return;  // uniform across the block
+    t0 = (int64_t)off[e] + 128 * local;
+    t_end = off[e + 1];
+    o_end = o0 + 128;
+  }
   const int tid = threadIdx.x;
   const int c16 = tid & 15;
   const int rb = tid >> 4;
@@ -186,7 +205,7 @@ __global__ __launch_bounds__(256) void k_quant_128x1(const uint16_t* __restrict_
   for (int j = 0; j < 8; ++j) {
     const int64_t t = t0 + rb * 8 + j;
     v[j] = make_uint4(0u, 0u, 0u, 0u);
-    if (t < T && avail > 0) v[j] = load_chunk8(x + t * ldx + col, avail);
+    if (t < t_end && avail > 0) v[j] = load_chunk8(x + t * ldx + col, avail);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -257,13 +276,13 @@ __global__ __launch_bounds__(256) void k_quant_128x1(const uint16_t* __restrict_
     const int sw = c >> 3;
     const uint2 lo = *reinterpret_cast<const uint2*>(tile + c * 128 + ((2 * part) ^ sw) * 8);
     const uint2 hi = *reinterpret_cast<const uint2*>(tile + c * 128 + ((2 * part + 1) ^ sw) * 8);
-    const int64_t t = t0 + 16 * part;
-    uint8_t* dst = qT + (c0 + c) * ldqT + t;
-    if (t + 16 <= T) {
+    const int64_t o = o0 + 16 * part;
+    uint8_t* dst = qT + (c0 + c) * ldqT + o;
+    if (o + 16 <= o_end) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     } else {
       const uint32_t wds[4] = {lo.x, lo.y, hi.x, hi.y};
-      for (int j = 0; j < 16 && t + j < T; ++j) dst[j] = (uint8_t)((wds[j >> 2] >> ((j & 3) * 8)) & 0xFF);
+      for (int j = 0; j < 16 && o + j < o_end; ++j) dst[j] = (uint8_t)((wds[j >> 2] >> ((j & 3) * 8)) & 0xFF);
     }
   }
 }
@@ -446,9 +465,37 @@ extern "C" fp8blk_status_t fp8blk_quantize_128x1(const uint16_t* x, int64_t T, i
   if (GC > 0x7FFFFFFF || GT > 65535) return FP8BLK_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)GC, (unsigned)GT);
   if (flags & FP8BLK_SCALE_POW2)
-    hipLaunchKernelGGL(k_quant_128x1<true>, grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT, s);
+    hipLaunchKernelGGL((k_quant_128x1<true, false>), grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT,
+                       s, nullptr, (int64_t)0);
   else
-    hipLaunchKernelGGL(k_quant_128x1<false>, grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT, s);
+    hipLaunchKernelGGL((k_quant_128x1<false, false>), grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT,
+                       s, nullptr, (int64_t)0);
+  return launch_status();
+}
+
+extern "C" int64_t fp8blk_token_group_slots(int64_t T, int64_t G) {
+  if (T < 0 || G < 0) return 0;
+  return T / 128 + G;
+}
+
+extern "C" fp8blk_status_t fp8blk_quantize_128x1_grouped(const uint16_t* x, int64_t T, int64_t C, int64_t ldx,
+                                                         int64_t G, const int32_t* group_offsets, uint8_t* qT,
+                                                         int64_t ldqT, float* s, uint32_t flags, void* stream) {
+  if (flags & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
+  if (T < 0 || C < 0 || G < 0 || !matrix_ok(x, T, C, ldx, 2)) return FP8BLK_ERR_INVALID_ARG;
+  if (T == 0 || C == 0 || G == 0) return FP8BLK_OK;  // no groups: nothing is written
+  const int64_t slots = fp8blk_token_group_slots(T, G);
+  if (!matrix_ok(qT, C, 128 * slots, ldqT, 1) || !vec_ok(s, slots * C)) return FP8BLK_ERR_INVALID_ARG;
+  if (group_offsets == nullptr || !aligned(group_offsets, 4)) return FP8BLK_ERR_INVALID_ARG;
+  const int64_t GC = ceil_div(C, 128);
+  if (GC > 0x7FFFFFFF || slots > 65535) return FP8BLK_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)GC, (unsigned)slots);
+  if (flags & FP8BLK_SCALE_POW2)
+    hipLaunchKernelGGL((k_quant_128x1<true, true>), grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT, s,
+                       group_offsets, G);
+  else
+    hipLaunchKernelGGL((k_quant_128x1<false, true>), grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT,
+                       s, group_offsets, G);
   return launch_status();
 }
 

@@ -205,6 +205,62 @@ fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(int64_t G, const int32_t* gr
                                                     void* workspace, size_t workspace_bytes,
                                                     void* stream);
 
+/*
+ * MoE backward, Wgrad operands: 128x1 quantization along tokens inside each
+ * expert's token range (the Wgrad operand tiling [p5¶4] applied per expert of
+ * the grouped projections [p2¶4]).  Expert e owns tokens
+ * [off[e], off[e+1]) of x; its tokens form ceil(M_e/128) groups of 128
+ * starting at its first token (M_e = off[e+1] - off[e]; the last group is
+ * partial when 128 does not divide M_e).  The groups of all experts are
+ * stored one after another: expert e's first group is slot
+ *   PG[e] = sum over e' < e of ceil(M_e'/128),
+ * and its token j is column 128*PG[e] + j of qT.
+ *   x   [T][C] BF16 (tokens in expert order), pitch ldx >= C.
+ *   group_offsets  DEVICE int32 [G+1], non-decreasing, off[0] = 0,
+ *                  off[G] = T.  Read on the device: no host sync.
+ *   qT  [C][128*S] E4M3 codes, pitch ldqT >= 128*S, S =
+ *       fp8blk_token_group_slots(T, G) (an upper bound on the number of
+ *       groups).  Columns of a partial group past the expert's last token
+ *       hold code 0; columns of slots past the last group are not written.
+ *   s   [S][C] FP32, dense: s[g*C + c] scales channel c over the tokens of
+ *       group slot g (rows of slots past the last group are not written).
+ *   Each group is quantized exactly as fp8blk_quantize_128x1 quantizes a
+ *   128-token tile of the expert's tokens.  flags: 0 or FP8BLK_SCALE_POW2.
+ *   FP8BLK_ERR_UNSUPPORTED if S > 65535.
+ */
+fp8blk_status_t fp8blk_quantize_128x1_grouped(const uint16_t* x, int64_t T, int64_t C, int64_t ldx,
+                                              int64_t G, const int32_t* group_offsets,
+                                              uint8_t* qT, int64_t ldqT, float* s, uint32_t flags,
+                                              void* stream);
+/* Group slots to allocate for T tokens in G experts: T/128 + G (integer
+ * division; 0 for negative arguments).  At least the number of ragged
+ * 128-token groups of any split of the T tokens into G experts. */
+int64_t fp8blk_token_group_slots(int64_t T, int64_t G);
+/*
+ * MoE backward, grouped Wgrad: for every expert e,
+ *   C_e[m][n] = sum over e's token groups g of sA[g][m] * sB[g][n] * P_g[m][n],
+ *   P_g[m][n] = sum over the tokens t of group g of dec(AT[m][t]) * dec(BT[n][t]),
+ * i.e. dW_e = X_e^T dY_e with both operands as written by
+ * fp8blk_quantize_128x1_grouped (same offsets, same T) [p5¶4; p2¶4].  Each
+ * group's partial is formed by the matrix cores and promoted into an FP32
+ * accumulator as in fp8blk_gemm_fp8_blockscaled (Wgrad role, ROW128 scales).
+ *   group_offsets  the DEVICE offsets given to the quantizer.
+ *   AT  [M][128*S] codes (pitch ldaT), sA [S][M]: X quantized, M = X's channels.
+ *   BT  [N][128*S] codes (pitch ldbT), sB [S][N]: dY quantized, N = dY's channels.
+ *   flags  0 or FP8BLK_GEMM_POW2_SCALES (every scale a power of two, e.g.
+ *          both operands quantized with FP8BLK_SCALE_POW2).
+ *   C   G matrices [M][N] FP32, expert e at C + e*strideC (floats),
+ *       pitch ldc >= N, strideC >= M*ldc and a multiple of 4; all
+ *       overwritten (an expert without tokens gets zeros).
+ *   ldaT, ldbT below 2^23 (FP8BLK_ERR_UNSUPPORTED otherwise).  With T = 0
+ *   the operands are not read (and may be NULL); C still gets zeros.
+ */
+fp8blk_status_t fp8blk_grouped_wgrad_fp8_blockscaled(int64_t G, const int32_t* group_offsets, int64_t T,
+                                                     int64_t M, int64_t N,
+                                                     const uint8_t* AT, int64_t ldaT, const float* sA,
+                                                     const uint8_t* BT, int64_t ldbT, const float* sB,
+                                                     uint32_t flags, float* C, int64_t ldc,
+                                                     int64_t strideC, void* stream);
 /* Workspace that lets fp8blk_gemm_fp8_blockscaled split K for this shape
  * (G = 1), for the current device; 0 when it would not split.  The grouped
  * GEMM (G > 1) needs none. */
@@ -213,7 +269,7 @@ size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
 /* Human-readable name of a status code (static string). */
 const char* fp8blk_status_string(fp8blk_status_t status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (2 added the MoE backward entry points). */
 int fp8blk_abi_version(void);
 
 #ifdef __cplusplus

@@ -365,6 +365,78 @@ def grouped_gemm_blockscaled(offsets: np.ndarray, A: np.ndarray, sA: np.ndarray,
     return C
 
 
+def token_group_starts(offsets) -> np.ndarray:
+    """Layout of the ragged 128-token groups of MoE experts (reading: the
+    pages tile Wgrad operands 128x1 along tokens [p5¶4] and run the expert
+    projections per expert [p2¶4]; tiling inside each expert's token range is
+    the plainest reading, and a group then never mixes two experts' tokens).
+    Expert e owns tokens [offsets[e], offsets[e+1]); they form
+    ceil(M_e/128) groups starting at its first token.  Returns PG int64
+    [G+1]: expert e's groups are slots PG[e] .. PG[e+1]-1, PG[G] the total."""
+    offsets = np.asarray(offsets, np.int64)
+    counts = -(-(offsets[1:] - offsets[:-1]) // TILE)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+
+
+def quantize_128x1_grouped(x_bits: np.ndarray, offsets, pow2: bool = False):
+    """128x1 quantization inside each expert's token range, in the slot
+    layout of ``token_group_starts``: expert e's token j is column
+    128*PG[e] + j.  x_bits: uint16 BF16 [T][C] (tokens in expert order).
+    Returns (qT uint8 [C][128*PG[G]], s float32 [PG[G]][C]); columns of a
+    partial last group past the expert's tokens hold code 0 (the code of
+    +0), so that they add nothing to a product."""
+    offsets = np.asarray(offsets, np.int64)
+    PG = token_group_starts(offsets)
+    C = x_bits.shape[1]
+    qT = np.zeros((C, TILE * int(PG[-1])), np.uint8)
+    s = np.empty((int(PG[-1]), C), np.float32)
+    for e in range(offsets.shape[0] - 1):
+        t0, t1 = int(offsets[e]), int(offsets[e + 1])
+        if t1 == t0:
+            continue
+        qe, se = quantize_128x1(x_bits[t0:t1], pow2)
+        c0 = TILE * int(PG[e])
+        qT[:, c0:c0 + (t1 - t0)] = qe
+        s[PG[e]:PG[e + 1]] = se
+    return qT, s
+
+
+def grouped_wgrad_blockscaled(offsets, AT: np.ndarray, sA: np.ndarray, BT: np.ndarray, sB: np.ndarray) -> np.ndarray:
+    """MoE grouped Wgrad: for each expert e, the Wgrad-role block-scaled GEMM
+    [p1¶3, p5¶4] over that expert's group slots only:
+      C_e[m,n] = sum over slots g of e of sA[g][m] * sB[g][n] * P_g[m,n],
+      P_g[m,n] = sum over the 128 columns t of slot g of dec(AT[m,t]) * dec(BT[n,t]).
+    AT [M][>=128*PG[G]], BT [N][>=128*PG[G]] codes and sA [>=PG[G]][M],
+    sB [>=PG[G]][N] as written by ``quantize_128x1_grouped``.  Returns
+    float64 [G][M][N]; an expert without tokens gets zeros."""
+    offsets = np.asarray(offsets, np.int64)
+    PG = token_group_starts(offsets)
+    Gn = offsets.shape[0] - 1
+    M, N = AT.shape[0], BT.shape[0]
+    out = np.zeros((Gn, M, N), np.float64)
+    for e in range(Gn):
+        g0, g1 = int(PG[e]), int(PG[e + 1])
+        if g1 == g0:
+            continue
+        cols = slice(TILE * g0, TILE * g1)
+        out[e] = gemm_blockscaled(AT[:, cols], sA[g0:g1], BT[:, cols], sB[g0:g1], OP_T, BSCALE_ROW128)
+    return out
+
+
+def grouped_wgrad_entries(offsets, AT, sA, BT, sB, experts, rows, cols) -> np.ndarray:
+    """The same sum as ``grouped_wgrad_blockscaled`` for selected entries
+    (experts[i], rows[i], cols[i]); used to check full-size outputs by
+    sampling."""
+    PG = token_group_starts(offsets)
+    out = np.zeros(len(experts), np.float64)
+    for i, (e, m, n) in enumerate(zip(experts, rows, cols)):
+        for g in range(int(PG[e]), int(PG[e + 1])):
+            ts = slice(TILE * g, TILE * (g + 1))
+            P = np.sum(e4m3_decode(AT[m, ts]) * e4m3_decode(BT[n, ts]))  # exact, see gemm_blockscaled
+            out[i] += P * (np.float64(sA[g, m]) * np.float64(sB[g, n]))
+    return out
+
+
 def gemm_unquantized(A_bits: np.ndarray, B_bits: np.ndarray, opB: int = OP_N) -> np.ndarray:
     """FP64 product of the BF16 inputs with no quantization; the reference
     for the accumulation/quantization error study."""

@@ -24,6 +24,12 @@ cast):
                    1000+e (up) or 2000+e (down) on the requested device.  seed 0
 * ``backward``     X [4096][7168] ~N(0,1); W [7168][2048] ~N(0,0.006);
                    dY [4096][2048] ~N(0,1e-3).                        seed 0
+* ``moe_grad``     MoE backward tensors over the expert-ordered rows of
+                   ``moe_routing``: "h" [rows][2048] ~N(0,1) (the down
+                   projection's input), "dout" [rows][7168] ~N(0,1e-3) (the
+                   gradient of its output), "dh" [rows][4096] ~N(0,1e-3) (the
+                   gradient of the up projection's output); each from its own
+                   generator seeded 3000/3001/3002 on the requested device.
 
 The hidden size 7168, the expert count 256 with top-8 routing and the expert
 width 2048 follow the DeepSeek-V3 description (inprokorea.com wr_id 890463,
@@ -37,7 +43,7 @@ import torch
 
 __all__ = [
     "bf16_bits", "randn_bf16", "single_gemm", "dense_fprop", "accum_study",
-    "moe_routing", "expert_weight", "backward", "edge_tensor",
+    "moe_routing", "expert_weight", "backward", "edge_tensor", "moe_grad",
 ]
 
 
@@ -109,6 +115,14 @@ def expert_weight(kind: str, e: int, device="cpu", K: int | None = None, N: int 
         raise ValueError(kind)
     g = torch.Generator(device=device).manual_seed(seed)
     return (torch.randn(K, N, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def moe_grad(kind: str, rows: int, device="cpu") -> torch.Tensor:
+    """MoE backward tensor ``kind`` ("h", "dout" or "dh") with ``rows``
+    expert-ordered rows, bf16, drawn on ``device``."""
+    seed, cols, std = {"h": (3000, 2048, 1.0), "dout": (3001, 7168, 1e-3), "dh": (3002, 4096, 1e-3)}[kind]
+    g = torch.Generator(device=device).manual_seed(seed)
+    return (torch.randn(rows, cols, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
 
 
 def backward():

@@ -36,7 +36,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fb.abi_version() == 1
+    assert fb.abi_version() == 2
+    assert fb.token_group_slots(65536, 256) == 512 + 256
+    assert fb.token_group_slots(100, 3) == 3 and fb.token_group_slots(-1, 3) == 0
     assert fb.status_string(0) == "FP8BLK_OK"
     assert fb.status_string(1) == "FP8BLK_ERR_INVALID_ARG"
     assert fb.status_string(2) == "FP8BLK_ERR_UNSUPPORTED"
@@ -130,6 +132,44 @@ def test_grouped_validation():
     assert call(opB=3) == INVALID
     assert call(G=-1) == INVALID
     assert call(G=0) == OK and call(Mt=0) == OK
+
+
+def test_grouped_128x1_validation():
+    f = fb.lib().fp8blk_quantize_128x1_grouped
+    T, G = 300, 4                      # 6 group slots: qT needs 768 columns
+
+    def call(T=T, C=256, ldx=256, G=G, off=FAKE, qT=FAKE, ldqT=768, s=FAKE, flags=0):
+        return f(FAKE, T, C, ldx, G, off, qT, ldqT, s, flags, NULL)
+
+    assert call(off=NULL) == INVALID
+    assert call(ldqT=752) == INVALID            # fewer columns than 128 slots
+    assert call(qT=NULL) == INVALID
+    assert call(s=NULL) == INVALID
+    assert call(flags=2) == INVALID
+    assert call(G=-1) == INVALID and call(T=-1) == INVALID
+    assert call(ldx=100) == INVALID
+    assert f(NULL, 0, 256, 256, G, FAKE, NULL, 512, NULL, 0, NULL) == OK   # no tokens
+    assert call(G=0, ldqT=256) == OK                                        # no experts
+
+
+def test_grouped_wgrad_validation():
+    f = fb.lib().fp8blk_grouped_wgrad_fp8_blockscaled
+    T, G, M, N = 300, 4, 128, 256      # 6 group slots: operands need 768 columns
+
+    def call(G=G, off=FAKE, T=T, M=M, N=N, A=FAKE, lda=768, sA=FAKE, B=FAKE, ldb=768, sB=FAKE, flags=0,
+             C=FAKE, ldc=256, sC=128 * 256):
+        return f(G, off, T, M, N, A, lda, sA, B, ldb, sB, flags, C, ldc, sC, NULL)
+
+    assert call(off=NULL) == INVALID
+    assert call(lda=640) == INVALID and call(ldb=640) == INVALID
+    assert call(A=NULL) == INVALID and call(B=NULL) == INVALID and call(C=NULL) == INVALID
+    assert call(sA=NULL) == INVALID and call(sB=NULL) == INVALID
+    assert call(sC=128 * 256 - 4) == INVALID    # experts' outputs would overlap
+    assert call(sC=128 * 256 + 2) == INVALID    # not 16-byte aligned per expert
+    assert call(flags=1) == INVALID
+    assert call(M=-1) == INVALID and call(T=-1) == INVALID
+    assert call(G=0) == OK and call(M=0) == OK and call(N=0) == OK
+    assert call(T=0, A=NULL, B=NULL, sA=NULL, sB=NULL, off=NULL) == INVALID   # C is still written
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
