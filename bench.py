@@ -273,6 +273,19 @@ def main():
                                             "gemm_us": round(t_g2 * 1e3, 2),
                                             "gemm_TFLOP/s": round(flops / t_g2 / 1e9, 1),
                                             "gemm_frac_mfma": round(flops / t_g2 / 1e9 / FP8_PEAK_TFLOPS, 4)}
+        # The step's GEMM with a BF16 output (the fused BF16 epilogue), over
+        # the same rotating input sets, fold and power-of-two paths.
+        Cb = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(S)]
+        for p2 in (False, True):
+            for j in range(S):
+                fb.quantize_1x128(A[j], pow2=p2, q=qA[j], s=sA[j])
+                fb.quantize_block128(W[j], pow2=p2, q=qW[j], s=sW[j])
+            t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qA[i % S], sA[i % S], qW[i % S], sW[i % S],
+                                                                      C=Cb[i % S], pow2_scales=p2), 40)
+            extras["fprop_gemm_bf16_out" + ("_pow2_scales" if p2 else "")] = {
+                "us": round(t * 1e3, 2), "TFLOP/s": round(flops / t / 1e9, 1),
+                "frac_mfma": round(flops / t / 1e9 / FP8_PEAK_TFLOPS, 4)}
+        del Cb
         extras.update(run_extras(torch, fb, synthetic, dev, np))
 
     cpu = None
@@ -449,7 +462,15 @@ def run_extras(torch, fb, synthetic, dev, np):
                                                         "GB/s": round(byts / t / 1e6, 1),
                                                         "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4),
                                                         "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
-    del Wd, AT, BT, sAT, sBT, dO, H
+    del Wd
+    torch.cuda.empty_cache()
+    Wb = torch.empty(G, 2048, Nd, dtype=torch.bfloat16, device=dev)
+    t = timed_events(torch, lambda i: fb.grouped_wgrad_fp8_blockscaled(offs, Mt, AT, sAT, BT, sBT, C=Wb), 3)
+    byts = G * 2048 * Nd * 2 + (2048 + Nd) * 128 * groups + 4 * groups * (2048 + Nd)
+    res["grouped_wgrad_down_2048x7168_T65536_E256_bf16_out"] = {
+        "us": round(t * 1e3, 1), "TFLOP/s": round(fl / t / 1e9, 1), "GB/s": round(byts / t / 1e6, 1),
+        "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4), "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
+    del Wb, AT, BT, sAT, sBT, dO, H
     torch.cuda.empty_cache()
     return res
 

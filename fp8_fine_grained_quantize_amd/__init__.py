@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "Fp8BlkError", "lib", "library_path", "OP_N", "OP_T", "BSCALE_BLOCK128", "BSCALE_ROW128",
-    "SCALE_POW2", "GEMM_POW2_SCALES", "quantize_1x128", "quantize_128x1", "quantize_block128",
+    "SCALE_POW2", "GEMM_POW2_SCALES", "GEMM_OUT_BF16", "quantize_1x128", "quantize_128x1", "quantize_block128",
     "requantize_128x1_from_1x128", "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled",
     "quantize_128x1_grouped", "token_group_slots", "grouped_wgrad_fp8_blockscaled",
     "workspace_bytes", "status_string", "abi_version", "EXPORTED_SYMBOLS", "empty_pitched", "as_pitched",
@@ -28,6 +28,7 @@ OP_N, OP_T = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 SCALE_POW2 = 0x1
 GEMM_POW2_SCALES = 0x100   # OR into opB: every scale is a power of two
+GEMM_OUT_BF16 = 0x200      # OR into opB (flags of the grouped Wgrad): C is BF16
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
 
@@ -195,17 +196,29 @@ def requantize_128x1_from_1x128(q: torch.Tensor, sq: torch.Tensor, pow2: bool = 
     return qT, sT
 
 
+def _out_flag(C, out_dtype):
+    dt = C.dtype if C is not None else out_dtype
+    if dt == torch.bfloat16:
+        return GEMM_OUT_BF16, torch.bfloat16, 2
+    if dt == torch.float32:
+        return 0, torch.float32, 4
+    raise TypeError(f"output must be float32 or bfloat16, got {dt}")
+
+
 def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCALE_BLOCK128, C=None,
-                         split_k: bool = True, workspace=None, pow2_scales: bool = False):
+                         split_k: bool = True, workspace=None, pow2_scales: bool = False,
+                         out_dtype=torch.float32):
     """C[M][N] float32 = block-scaled product of E4M3 codes A [M][K] and B
     ([K][N] for OP_N, [N][K] for OP_T); see the header for scale layouts.
     With split_k, a workspace of workspace_bytes(M, N, K) bytes is passed
     (allocated here unless given), which lets the library split K on shapes
     whose tiles cannot fill the GPU.  pow2_scales asserts that every scale is
-    a power of two (GEMM_POW2_SCALES)."""
+    a power of two (GEMM_POW2_SCALES).  out_dtype (or C's dtype) float32 or
+    bfloat16 (GEMM_OUT_BF16: the FP32 result rounded to nearest even)."""
     M, K = A.shape
     N = B.shape[1] if opB == OP_N else B.shape[0]
-    C = _empty_pitched(M, N, torch.float32, A.device, 4) if C is None else C
+    ob, odt, oel = _out_flag(C, out_dtype)
+    C = _empty_pitched(M, N, odt, A.device, oel) if C is None else C
     ws_ptr, ws_bytes = None, 0
     if split_k and M and N and K:
         need = workspace_bytes(M, N, K, 1)
@@ -214,14 +227,14 @@ def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCAL
                 workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=A.device)
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check(lib().fp8blk_gemm_fp8_blockscaled(M, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), _pitch(B),
-                                             opB | (GEMM_POW2_SCALES if pow2_scales else 0), _ptr(sB), bscale_mode,
+                                             opB | (GEMM_POW2_SCALES if pow2_scales else 0) | ob, _ptr(sB), bscale_mode,
                                              _ptr(C), _pitch(C), ws_ptr, ws_bytes, _stream()),
            "gemm_fp8_blockscaled")
     return C
 
 
 def grouped_gemm_fp8_blockscaled(offsets, A, sA, B, sB, opB: int = OP_N, max_group_rows=None, C=None,
-                                 pow2_scales: bool = False):
+                                 pow2_scales: bool = False, out_dtype=torch.float32):
     """Per-expert GEMM.  offsets: device int32 [G+1]; A [M_total][K];
     B [G][K][N] (OP_N) or [G][N][K] (OP_T) contiguous per expert; sB [G][...]."""
     G = offsets.numel() - 1
@@ -229,11 +242,12 @@ def grouped_gemm_fp8_blockscaled(offsets, A, sA, B, sB, opB: int = OP_N, max_gro
     N = B.shape[2] if opB == OP_N else B.shape[1]
     assert offsets.dtype == torch.int32 and offsets.is_cuda
     assert B.dim() == 3 and B.stride(2) == 1
-    C = _empty_pitched(M, N, torch.float32, A.device, 4) if C is None else C
+    ob, odt, oel = _out_flag(C, out_dtype)
+    C = _empty_pitched(M, N, odt, A.device, oel) if C is None else C
     mgr = M if max_group_rows is None else int(max_group_rows)
     _check(lib().fp8blk_grouped_gemm_fp8_blockscaled(
         G, _ptr(offsets), M, mgr, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), B.stride(1), B.stride(0),
-        opB | (GEMM_POW2_SCALES if pow2_scales else 0),
+        opB | (GEMM_POW2_SCALES if pow2_scales else 0) | ob,
         _ptr(sB), sB.stride(0), _ptr(C), _pitch(C), None, 0, _stream()), "grouped_gemm_fp8_blockscaled")
     return C
 
@@ -261,18 +275,20 @@ def quantize_128x1_grouped(x: torch.Tensor, offsets: torch.Tensor, pow2: bool = 
     return qT, s
 
 
-def grouped_wgrad_fp8_blockscaled(offsets: torch.Tensor, T: int, AT, sA, BT, sB, C=None, pow2_scales: bool = False):
+def grouped_wgrad_fp8_blockscaled(offsets: torch.Tensor, T: int, AT, sA, BT, sB, C=None, pow2_scales: bool = False,
+                                  out_dtype=torch.float32):
     """MoE grouped Wgrad: dW_e = X_e^T dY_e for every expert from the outputs
     of quantize_128x1_grouped of X (AT [M][128*S], sA) and of dY (BT
     [N][128*S], sB) with the same offsets and T.  Returns C float32 [G][M][N]."""
     G = offsets.numel() - 1
     assert offsets.dtype == torch.int32 and offsets.is_cuda
     M, N = AT.shape[0], BT.shape[0]
+    ob, odt, oel = _out_flag(C, out_dtype)
     if C is None:
-        C = torch.empty(G, M, _pad16(N, 4), dtype=torch.float32, device=AT.device)[:, :, :N]
+        C = torch.empty(G, M, _pad16(N, oel), dtype=odt, device=AT.device)[:, :, :N]
     assert C.dim() == 3 and C.stride(2) == 1
     _check(lib().fp8blk_grouped_wgrad_fp8_blockscaled(
         G, _ptr(offsets), T, M, N, _ptr(AT), _pitch(AT), _ptr(sA), _ptr(BT), _pitch(BT), _ptr(sB),
-        GEMM_POW2_SCALES if pow2_scales else 0, _ptr(C), C.stride(1), C.stride(0), _stream()),
+        (GEMM_POW2_SCALES if pow2_scales else 0) | ob, _ptr(C), C.stride(1), C.stride(0), _stream()),
         "grouped_wgrad_fp8_blockscaled")
     return C

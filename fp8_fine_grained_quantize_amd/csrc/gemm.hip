@@ -167,6 +167,19 @@ __device__ __forceinline__ void dma4(v4i r, uint32_t voff, uint8_t* lds_base) {
                : "memory", "m0");
 }
 
+// BF16 bits of an FP32 value, rounded to nearest even (a NaN stays a quiet
+// NaN; values beyond the largest finite BF16 round to infinity).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Row `row` of an output matrix of FP32 or BF16 elements.
+__device__ __forceinline__ void* out_row(void* C, int64_t ldc, int64_t row, bool bf16) {
+  return static_cast<char*>(C) + row * ldc * (bf16 ? 2 : 4);
+}
+
 // Arguments of one output tile: where its operands start and how far they
 // extend.  The dense kernel and the grouped kernel both build one of these.
 struct TileArgs {
@@ -180,8 +193,8 @@ struct TileArgs {
   int64_t n0, N;
   const float* sB;    // scale table of this B
   int64_t sB_ld;      // row length of the scale table
-  float* C;           // C + m0 * ldc
-  int64_t ldc;
+  void* C;            // row m0 of C (FP32, or BF16 for the OB kernels)
+  int64_t ldc;        // row pitch of C in elements
   int64_t K;
   int g0, g1;         // K groups [g0, g1) of this tile's (partial) product
 };
@@ -200,10 +213,9 @@ struct CopyPlan {
   // cover both.
   static constexpr int KSTEP = NW * 64 / (BN / 16);
   static_assert(KSTEP % 32 == 0, "[K][N] copies: bit 5 of k per lane or alternating per iteration");
-  uint32_t a, b, b2, sc;
+  uint32_t a, b, b2;
 
   __device__ __forceinline__ void init(const TileArgs& t) {
-    constexpr int TM = CFG::TM, WTM = CFG::WTM;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     {  // A and [N][K] B: chunk ci = (it*NW + wave)*64 + lane; row ci/8 advances by 8*NW per it
@@ -221,21 +233,30 @@ struct CopyPlan {
       b = (uint32_t)(k * t.ldb + (p16 ^ nmaj_swz<BN>(k)) * 16);
       b2 = KSTEP % 64 == 0 ? b : (uint32_t)(k * t.ldb + (p16 ^ nmaj_swz<BN>(k ^ 32)) * 16);
     }
-    int blk = wave;
+  }
+
+  // Per-lane byte offset of this lane's scale copy, recomputed at each issue
+  // from an opaque copy of the thread id: a few integer operations per group,
+  // one VGPR less held across the K loop (the 256x256 fold kernels run at
+  // the register limit).
+  __device__ __forceinline__ uint32_t sc_offset(const TileArgs& t) const {
+    constexpr int TM = CFG::TM, WTM = CFG::WTM;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    int blk = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (blk >= CFG::S_BLOCKS) blk = 0;  // surplus copy: rewrites block 0 with the same data
     const int p = blk * 64 + lane;      // float position in the [BM + BN] scale buffer
     // BM is a multiple of 64, so the row/column choice is uniform per wave
     // (derived from blk alone), which keeps the resource in scalar registers.
     if (blk * 64 < BM) {
       const int w = p / WTM, q = p % WTM;
-      sc = (uint32_t)((w * WTM + 16 * (q % TM) + q / TM) * 4);
-    } else if (ROW128) {
-      sc = (uint32_t)((p - BM) * 4);  // column scale of column n0 + (p - BM)
-    } else {
-      // block scale of column block n0/128 + (p - BM); only the first BN/128
-      // positions are used
-      sc = (uint32_t)((p - BM) * (OPB_T ? t.K / 128 : 1) * 4);
+      return (uint32_t)((w * WTM + 16 * (q % TM) + q / TM) * 4);
     }
+    if (ROW128) return (uint32_t)((p - BM) * 4);  // column scale of column n0 + (p - BM)
+    // block scale of column block n0/128 + (p - BM); only the first BN/128
+    // positions are used
+    return (uint32_t)((p - BM) * (OPB_T ? t.K / 128 : 1) * 4);
   }
 
   __device__ __forceinline__ void issue(const TileArgs& t, int g, uint8_t* buf, float* sbuf) const {
@@ -287,7 +308,7 @@ struct CopyPlan {
       const int blk = wave < CFG::S_BLOCKS ? wave : 0;
       const bool rows = blk * 64 < BM;  // wave-uniform; a select keeps the copy branch-free
       const v4i rs = v4i{rows ? rsa[0] : rsb[0], rows ? rsa[1] : rsb[1], rows ? rsa[2] : rsb[2], rows ? rsa[3] : rsb[3]};
-      dma4(rs, sc, (uint8_t*)(sbuf + blk * 64));
+      dma4(rs, sc_offset(t), (uint8_t*)(sbuf + blk * 64));
     }
   }
 };
@@ -489,13 +510,9 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
 // LDS arrays (the two pipeline stages); the loop is unrolled by two so that
 // every access names its array at compile time, which lets the compiler see
 // that reading one stage does not have to wait for copies into the other.
-template <class CFG, bool OPB_T, bool ROW128, bool P2>
+template <class CFG, bool OPB_T, bool ROW128, bool P2, bool OB>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint8_t* ops1, float* sc0, float* sc1) {
   constexpr int TM = CFG::TM, TN = CFG::TN;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
-  const int l16 = lane & 15, lq = lane >> 4;
   const int g0 = t.g0, G = t.g1;
 
   constexpr bool ILV = interleaved_copies<CFG, P2>();
@@ -532,15 +549,46 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
 
   if (ILV) wait_vmcnt<0>();  // the last group's (empty) interleaved copies
 
-  // ---- epilogue: FP32 C, four consecutive columns per lane ----
+  // ---- epilogue: four consecutive columns per lane, FP32 or (OB) BF16 ----
+  // The BF16 store derives the lane's row/column position afresh from the
+  // thread id (an opaque copy keeps the compiler from holding the loop-entry
+  // values in registers across the K loop, which made the 256x256 fold kernel
+  // spill inside the loop).
+  int tid_e = threadIdx.x;
+  if constexpr (OB) asm volatile("" : "+v"(tid_e));
+  const int wm_e = (tid_e >> 6) / CFG::WAVES_N, wn_e = (tid_e >> 6) % CFG::WAVES_N;
+  const int l16_e = tid_e & 15, lq_e = (tid_e >> 4) & 3;
+  if constexpr (OB) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
+      if (row >= t.rows) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = t.n0 + wn_e * CFG::WTN + 16 * j + 4 * lq_e;
+        uint16_t* dst = static_cast<uint16_t*>(t.C) + row * t.ldc + col;
+        const uint32_t b0 = bf16_rne(acc[i][j][0]), b1 = bf16_rne(acc[i][j][1]);
+        const uint32_t b2 = bf16_rne(acc[i][j][2]), b3 = bf16_rne(acc[i][j][3]);
+        if (col + 3 < t.N) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        } else {
+          const uint32_t b[4] = {b0, b1, b2, b3};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col + r < t.N) dst[r] = (uint16_t)b[r];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t row = wm * CFG::WTM + 16 * i + l16;
+    const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
     if (row >= t.rows) continue;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int64_t col = t.n0 + wn * CFG::WTN + 16 * j + 4 * lq;
-      float* dst = t.C + row * t.ldc + col;
+      const int64_t col = t.n0 + wn_e * CFG::WTN + 16 * j + 4 * lq_e;
+      float* dst = static_cast<float*>(t.C) + row * t.ldc + col;
       if (col + 3 < t.N) {
         *reinterpret_cast<float4*>(dst) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       } else {
@@ -578,12 +626,12 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nblocks, int64_t ti
   tn = in / gm;
 }
 
-template <class CFG, bool OPB_T, bool ROW128, bool P2>
+template <class CFG, bool OPB_T, bool ROW128, bool P2, bool OB>
 __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
                                                    int64_t lda, const float* __restrict__ sA,
                                                    const uint8_t* __restrict__ B, int64_t ldb,
                                                    const float* __restrict__ sB, int64_t sB_ld,
-                                                   float* __restrict__ C, int64_t ldc, int64_t tiles_m,
+                                                   void* __restrict__ C, int64_t ldc, int64_t tiles_m,
                                                    int64_t tiles_n, float* __restrict__ partials, int groups_per_split) {
   FP8BLK_DECLARE_STAGES(CFG);
   int64_t tm, tn;
@@ -591,6 +639,8 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
   // Split K: workgroup row blockIdx.y computes the partial product of K
   // groups [y*groups_per_split, ...) into its own [M][N] slice of `partials`.
   const int G = (int)(K / 128);
+  // (OB kernels are never split: a split GEMM writes FP32 partials and the
+  // reduction writes BF16.)
   const int split = blockIdx.y;
   if (gridDim.y > 1) {
     C = partials + (int64_t)split * M * N;
@@ -609,12 +659,12 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
   t.N = N;
   t.sB = sB;
   t.sB_ld = sB_ld;
-  t.C = C + m0 * ldc;
+  t.C = out_row(C, ldc, m0, OB);
   t.ldc = ldc;
   t.K = K;
   t.g0 = split * groups_per_split;
   t.g1 = t.g0 + groups_per_split < G ? t.g0 + groups_per_split : G;
-  gemm_tile<CFG, OPB_T, ROW128, P2>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, OPB_T, ROW128, P2, OB>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Grouped: tiles are enumerated expert by expert, within an expert column
@@ -622,7 +672,7 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
 // workgroups share each expert's weight tile.  The per-expert row counts are
 // read from the device-resident offsets (prefix scan in LDS), so the host
 // never synchronizes; surplus workgroups of the upper-bound grid exit.
-template <class CFG, bool OPB_T, bool P2>
+template <class CFG, bool OPB_T, bool P2, bool OB>
 __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32_t* __restrict__ offsets,
                                                            int64_t M_total, int64_t N, int64_t K,
                                                            const uint8_t* __restrict__ A, int64_t lda,
@@ -630,7 +680,7 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
                                                            const uint8_t* __restrict__ B, int64_t ldb,
                                                            int64_t strideB, const float* __restrict__ sB,
                                                            int64_t stride_sB, int64_t sB_ld,
-                                                           float* __restrict__ C, int64_t ldc, int64_t tiles_n) {
+                                                           void* __restrict__ C, int64_t ldc, int64_t tiles_n) {
   FP8BLK_DECLARE_STAGES(CFG);
   __shared__ int64_t s_tile_base[CFG::NT + 1];
   __shared__ int64_t s_found[2];
@@ -694,12 +744,12 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   t.N = N;
   t.sB = sB + e * stride_sB;
   t.sB_ld = sB_ld;
-  t.C = C + m0 * ldc;
+  t.C = out_row(C, ldc, m0, OB);
   t.ldc = ldc;
   t.K = K;
   t.g0 = 0;
   t.g1 = (int)(K / 128);
-  gemm_tile<CFG, OPB_T, false, P2>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, OPB_T, false, P2, OB>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Grouped Wgrad of MoE experts: dW_e = X_e^T dY_e for every expert e, both
@@ -709,12 +759,12 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
 // Every expert's output has the same M x N tiles; tiles are enumerated expert
 // by expert, column tile by column tile, row tiles innermost.  An expert
 // without tokens gets dW_e = 0.
-template <class CFG, bool P2>
+template <class CFG, bool P2, bool OB>
 __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __restrict__ offsets, int64_t M, int64_t N,
                                                             const uint8_t* __restrict__ A, int64_t lda,
                                                             const float* __restrict__ sA,
                                                             const uint8_t* __restrict__ B, int64_t ldb,
-                                                            const float* __restrict__ sB, float* __restrict__ C,
+                                                            const float* __restrict__ sB, void* __restrict__ C,
                                                             int64_t ldc, int64_t strideC, int64_t tiles_m,
                                                             int64_t tiles_n) {
   FP8BLK_DECLARE_STAGES(CFG);
@@ -738,39 +788,53 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __rest
   t.N = N;
   t.sB = sB;
   t.sB_ld = N;
-  t.C = C + e * strideC + m0 * ldc;
+  t.C = out_row(out_row(C, strideC, e, OB), ldc, m0, OB);
   t.ldc = ldc;
   t.K = 128 * (pg + ng);
   t.g0 = (int)pg;
   t.g1 = (int)(pg + ng);
-  gemm_tile<CFG, true, true, P2>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, true, true, P2, OB>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Split-K reduction: C[m][n] = sum over s = 0 .. S-1, in that order, of the
 // partial products partials[s][m][n] (FP32 additions).  Four consecutive
 // columns per thread.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partials, int S, int64_t M,
-                                                       int64_t N, float* __restrict__ C, int64_t ldc) {
+                                                       int64_t N, void* __restrict__ Cv, int64_t ldc, int out_bf16) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index of a 4-column chunk
   const int64_t cpr = (N + 3) / 4;
   const int64_t m = q / cpr, n = (q % cpr) * 4;
   if (m >= M) return;
   const int64_t MN = M * N;
   const float* src = partials + m * N + n;
-  float* dst = C + m * ldc + n;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (n + 4 <= N && (N & 3) == 0) {
-    float4 acc = *reinterpret_cast<const float4*>(src);
+    float4 a = *reinterpret_cast<const float4*>(src);
     for (int s = 1; s < S; ++s) {
       const float4 v = *reinterpret_cast<const float4*>(src + s * MN);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
     }
-    *reinterpret_cast<float4*>(dst) = acc;
+    acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
   } else {
     for (int r = 0; r < 4 && n + r < N; ++r) {
-      float acc = src[r];
-      for (int s = 1; s < S; ++s) acc += src[s * MN + r];
-      dst[r] = acc;
+      float a = src[r];
+      for (int s = 1; s < S; ++s) a += src[s * MN + r];
+      acc[r] = a;
     }
+  }
+  if (out_bf16) {
+    uint16_t* dst = static_cast<uint16_t*>(Cv) + m * ldc + n;
+    if (n + 4 <= N)
+      *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16),
+                                                  bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16));
+    else
+      for (int r = 0; r < 4 && n + r < N; ++r) dst[r] = (uint16_t)bf16_rne(acc[r]);
+  } else {
+    float* dst = static_cast<float*>(Cv) + m * ldc + n;
+    if (n + 4 <= N)
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    else
+      for (int r = 0; r < 4 && n + r < N; ++r) dst[r] = acc[r];
   }
 }
 
@@ -795,21 +859,25 @@ static size_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
 
 template <class CFG, bool OPB_T, bool ROW128, bool P2>
 static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
-                                    const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_ld, float* C,
-                                    int64_t ldc, float* partials, int64_t S, hipStream_t stream) {
+                                    const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_ld, void* C,
+                                    int64_t ldc, int out_bf16, float* partials, int64_t S, hipStream_t stream) {
   const int64_t tiles_m = ceil_div(M, CFG::BM), tiles_n = ceil_div(N, CFG::BN);
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
   const int64_t G = K / 128;
   const int64_t per = ceil_div(G, S);
   S = ceil_div(G, per);  // no empty split
-  hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2>), dim3((unsigned)blocks, (unsigned)S), dim3(CFG::NT), 0, stream, M, N,
-                     K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per);
+  if (out_bf16 && S == 1)
+    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2, true>), dim3((unsigned)blocks), dim3(CFG::NT), 0, stream, M, N,
+                       K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per);
+  else
+    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2, false>), dim3((unsigned)blocks, (unsigned)S), dim3(CFG::NT), 0,
+                       stream, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per);
   if (S > 1) {
     if (hipGetLastError() != hipSuccess) return FP8BLK_ERR_LAUNCH;
     const int64_t chunks = M * ceil_div(N, 4);
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(chunks, 256)), dim3(256), 0, stream, partials, (int)S,
-                       M, N, C, ldc);
+                       M, N, C, ldc, out_bf16);
   }
   return launch_status();
 }
@@ -817,14 +885,14 @@ static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8
 template <class CFG, bool ROW128>
 static fp8blk_status_t dispatch_dense(bool t, bool p2, int64_t M, int64_t N, int64_t K, const uint8_t* A,
                                       int64_t lda, const float* sA, const uint8_t* B, int64_t ldb, const float* sB,
-                                      int64_t sB_ld, float* C, int64_t ldc, float* partials, int64_t S,
+                                      int64_t sB_ld, void* C, int64_t ldc, int ob, float* partials, int64_t S,
                                       hipStream_t st) {
   if (p2) {
-    if (t) return launch_dense<CFG, true, ROW128, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
-    return launch_dense<CFG, false, ROW128, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+    if (t) return launch_dense<CFG, true, ROW128, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
+    return launch_dense<CFG, false, ROW128, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   }
-  if (t) return launch_dense<CFG, true, ROW128, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
-  return launch_dense<CFG, false, ROW128, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+  if (t) return launch_dense<CFG, true, ROW128, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
+  return launch_dense<CFG, false, ROW128, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
 }
 
 }  // namespace fp8blk
@@ -843,17 +911,18 @@ extern "C" size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_
 
 extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                                                        const float* sA, const uint8_t* B, int64_t ldb, int opB,
-                                                       const float* sB, int bscale_mode, float* C, int64_t ldc,
+                                                       const float* sB, int bscale_mode, void* C, int64_t ldc,
                                                        void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0) return FP8BLK_ERR_INVALID_ARG;
   const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
-  opB &= ~FP8BLK_GEMM_POW2_SCALES;
+  const int ob = (opB & FP8BLK_GEMM_OUT_BF16) != 0;
+  opB &= ~(FP8BLK_GEMM_POW2_SCALES | FP8BLK_GEMM_OUT_BF16);
   if (opB != FP8BLK_OP_N && opB != FP8BLK_OP_T) return FP8BLK_ERR_INVALID_ARG;
   if (bscale_mode != FP8BLK_BSCALE_BLOCK128 && bscale_mode != FP8BLK_BSCALE_ROW128) return FP8BLK_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP8BLK_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FP8BLK_OK;
   if (K == 0) return FP8BLK_ERR_INVALID_ARG;
-  if (!matrix_ok(A, M, K, lda, 1) || !matrix_ok(C, M, N, ldc, 4)) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(A, M, K, lda, 1) || !matrix_ok(C, M, N, ldc, ob ? 2 : 4)) return FP8BLK_ERR_INVALID_ARG;
   if (opB == FP8BLK_OP_N ? !matrix_ok(B, K, N, ldb, 1) : !matrix_ok(B, N, K, ldb, 1)) return FP8BLK_ERR_INVALID_ARG;
   if (lda >= kMaxPitch || ldb >= kMaxPitch) return FP8BLK_ERR_UNSUPPORTED;
   const int64_t G = K / 128;
@@ -884,19 +953,19 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
   if (bscale_mode == FP8BLK_BSCALE_ROW128) {
     const int64_t row_tiles = ceil_div(M, RowCfg::BM) * ceil_div(N, RowCfg::BN);
     if (row_tiles >= 128)
-      return dispatch_dense<RowCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
-    return dispatch_dense<SmallCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+      return dispatch_dense<RowCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
+    return dispatch_dense<SmallCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   }
   const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
   if (big_tiles >= 128)
-    return dispatch_dense<BigCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
-  return dispatch_dense<SmallCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, partials, S, st);
+    return dispatch_dense<BigCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
+  return dispatch_dense<SmallCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
 }
 
 extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
     int64_t G, const int32_t* group_offsets, int64_t M_total, int64_t max_group_rows, int64_t N, int64_t K,
     const uint8_t* A, int64_t lda, const float* sA, const uint8_t* B, int64_t ldb, int64_t strideB, int opB,
-    const float* sB, int64_t stride_sB, float* C, int64_t ldc, void* workspace, size_t workspace_bytes,
+    const float* sB, int64_t stride_sB, void* C, int64_t ldc, void* workspace, size_t workspace_bytes,
     void* stream) {
   (void)workspace;
   (void)workspace_bytes;
@@ -906,12 +975,13 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   using CFG = SmallCfg;
   if (G < 0 || M_total < 0 || N < 0 || K < 0 || max_group_rows < 0) return FP8BLK_ERR_INVALID_ARG;
   const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
-  opB &= ~FP8BLK_GEMM_POW2_SCALES;
+  const int ob = (opB & FP8BLK_GEMM_OUT_BF16) != 0;
+  opB &= ~(FP8BLK_GEMM_POW2_SCALES | FP8BLK_GEMM_OUT_BF16);
   if (opB != FP8BLK_OP_N && opB != FP8BLK_OP_T) return FP8BLK_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP8BLK_ERR_INVALID_ARG;
   if (G == 0 || M_total == 0 || N == 0) return FP8BLK_OK;
   if (K == 0 || group_offsets == nullptr || !aligned(group_offsets, 4)) return FP8BLK_ERR_INVALID_ARG;
-  if (!matrix_ok(A, M_total, K, lda, 1) || !matrix_ok(C, M_total, N, ldc, 4)) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(A, M_total, K, lda, 1) || !matrix_ok(C, M_total, N, ldc, ob ? 2 : 4)) return FP8BLK_ERR_INVALID_ARG;
   const int64_t Gk = K / 128, NB = ceil_div(N, 128);
   const int64_t brows = opB == FP8BLK_OP_N ? K : N, bcols = opB == FP8BLK_OP_N ? N : K;
   if (!matrix_ok(B, brows, bcols, ldb, 1)) return FP8BLK_ERR_INVALID_ARG;
@@ -932,14 +1002,17 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   if (blocks % 8) blocks += 8 - blocks % 8;  // keep the XCD remap a bijection on the grid
   if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
   hipStream_t st = as_stream(stream);
-#define FP8BLK_GROUPED_LAUNCH(T_, P2_)                                                                         \
-  hipLaunchKernelGGL((k_grouped_gemm<CFG, T_, P2_>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G, group_offsets, \
-                     M_total, N, K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n)
+#define FP8BLK_GROUPED_LAUNCH(T_, P2_, OB_)                                                                      \
+  hipLaunchKernelGGL((k_grouped_gemm<CFG, T_, P2_, OB_>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G,          \
+                     group_offsets, M_total, N, K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n)
+#define FP8BLK_GROUPED_LAUNCH_OB(T_, P2_) \
+  if (ob) FP8BLK_GROUPED_LAUNCH(T_, P2_, true); else FP8BLK_GROUPED_LAUNCH(T_, P2_, false)
   if (opB == FP8BLK_OP_T) {
-    if (p2) FP8BLK_GROUPED_LAUNCH(true, true); else FP8BLK_GROUPED_LAUNCH(true, false);
+    if (p2) { FP8BLK_GROUPED_LAUNCH_OB(true, true); } else { FP8BLK_GROUPED_LAUNCH_OB(true, false); }
   } else {
-    if (p2) FP8BLK_GROUPED_LAUNCH(false, true); else FP8BLK_GROUPED_LAUNCH(false, false);
+    if (p2) { FP8BLK_GROUPED_LAUNCH_OB(false, true); } else { FP8BLK_GROUPED_LAUNCH_OB(false, false); }
   }
+#undef FP8BLK_GROUPED_LAUNCH_OB
 #undef FP8BLK_GROUPED_LAUNCH
   return launch_status();
 }
@@ -948,14 +1021,15 @@ extern "C" fp8blk_status_t fp8blk_grouped_wgrad_fp8_blockscaled(int64_t G, const
                                                                 int64_t M, int64_t N, const uint8_t* AT,
                                                                 int64_t ldaT, const float* sA, const uint8_t* BT,
                                                                 int64_t ldbT, const float* sB, uint32_t flags,
-                                                                float* C, int64_t ldc, int64_t strideC,
+                                                                void* C, int64_t ldc, int64_t strideC,
                                                                 void* stream) {
   // 128 x 128 tiles: the per-column scales of both operands (ROW128) need the
   // registers of the smaller tile.
   using CFG = RowCfg;
   if (G < 0 || T < 0 || M < 0 || N < 0) return FP8BLK_ERR_INVALID_ARG;
-  if (flags & ~(uint32_t)FP8BLK_GEMM_POW2_SCALES) return FP8BLK_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(FP8BLK_GEMM_POW2_SCALES | FP8BLK_GEMM_OUT_BF16)) return FP8BLK_ERR_INVALID_ARG;
   const bool p2 = (flags & FP8BLK_GEMM_POW2_SCALES) != 0;
+  const int ob = (flags & FP8BLK_GEMM_OUT_BF16) != 0;
   if (G == 0 || M == 0 || N == 0) return FP8BLK_OK;
   const int64_t slots = fp8blk_token_group_slots(T, G);
   if (group_offsets == nullptr || !aligned(group_offsets, 4)) return FP8BLK_ERR_INVALID_ARG;
@@ -964,17 +1038,21 @@ extern "C" fp8blk_status_t fp8blk_grouped_wgrad_fp8_blockscaled(int64_t G, const
       return FP8BLK_ERR_INVALID_ARG;
     if (!vec_ok(sA, slots * M) || !vec_ok(sB, slots * N)) return FP8BLK_ERR_INVALID_ARG;
   }
-  if (!matrix_ok(C, M, N, ldc, 4) || strideC < M * ldc || strideC % 4 != 0) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(C, M, N, ldc, ob ? 2 : 4) || strideC < M * ldc || strideC % (ob ? 8 : 4) != 0)
+    return FP8BLK_ERR_INVALID_ARG;
   if (ldaT >= kMaxPitch || ldbT >= kMaxPitch || slots > 0x7FFFFFFF / 2) return FP8BLK_ERR_UNSUPPORTED;
   const int64_t tiles_m = ceil_div(M, CFG::BM), tiles_n = ceil_div(N, CFG::BN);
   const int64_t blocks = G * tiles_m * tiles_n;
   if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
   hipStream_t st = as_stream(stream);
-  if (p2)
-    hipLaunchKernelGGL((k_grouped_wgrad<CFG, true>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, group_offsets, M, N,
-                       AT, ldaT, sA, BT, ldbT, sB, C, ldc, strideC, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((k_grouped_wgrad<CFG, false>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, group_offsets, M,
-                       N, AT, ldaT, sA, BT, ldbT, sB, C, ldc, strideC, tiles_m, tiles_n);
+#define FP8BLK_WGRAD_LAUNCH(P2_, OB_)                                                                             \
+  hipLaunchKernelGGL((k_grouped_wgrad<CFG, P2_, OB_>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, group_offsets, M, \
+                     N, AT, ldaT, sA, BT, ldbT, sB, C, ldc, strideC, tiles_m, tiles_n)
+  if (p2) {
+    if (ob) FP8BLK_WGRAD_LAUNCH(true, true); else FP8BLK_WGRAD_LAUNCH(true, false);
+  } else {
+    if (ob) FP8BLK_WGRAD_LAUNCH(false, true); else FP8BLK_WGRAD_LAUNCH(false, false);
+  }
+#undef FP8BLK_WGRAD_LAUNCH
   return launch_status();
 }

@@ -80,6 +80,13 @@ enum { FP8BLK_OP_N = 0, /* B stored [K][N] (row pitch ldb >= N)            */
  * a power of two is read as 2^(its biased exponent - 127): the result is
  * then wrong, not an error. */
 #define FP8BLK_GEMM_POW2_SCALES 0x100
+/* Flag OR'ed into `opB` of the dense and grouped GEMMs (and into `flags` of
+ * the grouped Wgrad): C is BF16 instead of FP32.  Each output is the same
+ * FP32 result rounded to the nearest BF16 (ties to even; NaN stays NaN,
+ * values beyond the BF16 range become infinities).  C then holds uint16_t
+ * BF16 bit patterns, its pitch ldc (and strideC) counts BF16 elements, and
+ * the alignment rules apply to the BF16 matrix (pitch a multiple of 8). */
+#define FP8BLK_GEMM_OUT_BF16 0x200
 
 /* B scale layouts */
 enum { FP8BLK_BSCALE_BLOCK128 = 0, /* one scale per 128x128 block of B as stored:
@@ -151,7 +158,8 @@ fp8blk_status_t fp8blk_requantize_128x1_from_1x128(const uint8_t* q, const float
  *   A  [M][K] E4M3 codes, pitch lda >= K; sA [K/128][M] FP32 (1x128 scales).
  *   B  [K][N] (opB = FP8BLK_OP_N, pitch ldb >= N) or [N][K] (FP8BLK_OP_T,
  *      pitch ldb >= K) E4M3 codes; sB per `bscale_mode`.
- *   C  [M][N] FP32, pitch ldc >= N (overwritten).
+ *   C  [M][N] FP32 (BF16 with FP8BLK_GEMM_OUT_BF16), pitch ldc >= N
+ *      (overwritten).
  *   K must be a positive multiple of 128 (M, N arbitrary); lda and ldb
  *   must be below 2^23 (FP8BLK_ERR_UNSUPPORTED otherwise).
  *   Roles: Fprop Y = X W (A = 1x128-quantized X, B = W [K][N] block-scaled,
@@ -173,7 +181,7 @@ fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                             const uint8_t* A, int64_t lda, const float* sA,
                                             const uint8_t* B, int64_t ldb, int opB,
                                             const float* sB, int bscale_mode,
-                                            float* C, int64_t ldc,
+                                            void* C, int64_t ldc,
                                             void* workspace, size_t workspace_bytes,
                                             void* stream);
 
@@ -190,7 +198,7 @@ fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
  *       (OP_N, pitch ldb >= N) or [N][K] (OP_T, pitch ldb >= K).
  *   sB  G block-scale tables (BLOCK128 layout of one B_e), expert e at
  *       sB + e*stride_sB (floats).
- *   C   [M_total][N] FP32, pitch ldc.
+ *   C   [M_total][N] FP32 (BF16 with FP8BLK_GEMM_OUT_BF16), pitch ldc.
  *   max_group_rows: an upper bound on any group's row count (e.g. M_total),
  *   or 0 if unknown; it only sizes the launch grid.
  *   K must be a positive multiple of 128; lda, ldb below 2^23.
@@ -201,7 +209,7 @@ fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(int64_t G, const int32_t* gr
                                                     const uint8_t* A, int64_t lda, const float* sA,
                                                     const uint8_t* B, int64_t ldb, int64_t strideB,
                                                     int opB, const float* sB, int64_t stride_sB,
-                                                    float* C, int64_t ldc,
+                                                    void* C, int64_t ldc,
                                                     void* workspace, size_t workspace_bytes,
                                                     void* stream);
 
@@ -247,11 +255,13 @@ int64_t fp8blk_token_group_slots(int64_t T, int64_t G);
  *   group_offsets  the DEVICE offsets given to the quantizer.
  *   AT  [M][128*S] codes (pitch ldaT), sA [S][M]: X quantized, M = X's channels.
  *   BT  [N][128*S] codes (pitch ldbT), sB [S][N]: dY quantized, N = dY's channels.
- *   flags  0 or FP8BLK_GEMM_POW2_SCALES (every scale a power of two, e.g.
- *          both operands quantized with FP8BLK_SCALE_POW2).
- *   C   G matrices [M][N] FP32, expert e at C + e*strideC (floats),
- *       pitch ldc >= N, strideC >= M*ldc and a multiple of 4; all
- *       overwritten (an expert without tokens gets zeros).
+ *   flags  0, or FP8BLK_GEMM_POW2_SCALES (every scale a power of two, e.g.
+ *          both operands quantized with FP8BLK_SCALE_POW2) and/or
+ *          FP8BLK_GEMM_OUT_BF16.
+ *   C   G matrices [M][N] FP32 (BF16 with FP8BLK_GEMM_OUT_BF16), expert e
+ *       at C + e*strideC elements, pitch ldc >= N, strideC >= M*ldc and
+ *       16-byte aligned; all overwritten (an expert without tokens gets
+ *       zeros).
  *   ldaT, ldbT below 2^23 (FP8BLK_ERR_UNSUPPORTED otherwise).  With T = 0
  *   the operands are not read (and may be NULL); C still gets zeros.
  */
@@ -259,7 +269,7 @@ fp8blk_status_t fp8blk_grouped_wgrad_fp8_blockscaled(int64_t G, const int32_t* g
                                                      int64_t M, int64_t N,
                                                      const uint8_t* AT, int64_t ldaT, const float* sA,
                                                      const uint8_t* BT, int64_t ldbT, const float* sB,
-                                                     uint32_t flags, float* C, int64_t ldc,
+                                                     uint32_t flags, void* C, int64_t ldc,
                                                      int64_t strideC, void* stream);
 /* Workspace that lets fp8blk_gemm_fp8_blockscaled split K for this shape
  * (G = 1), for the current device; 0 when it would not split.  The grouped

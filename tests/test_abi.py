@@ -116,6 +116,8 @@ def test_gemm_validation():
     assert _gemm(opB=1, ldb=128) == INVALID    # [N][K] needs ldb >= K
     assert _gemm(A=MIS) == INVALID
     assert _gemm(M=0) == OK and _gemm(N=0) == OK
+    assert _gemm(opB=0x200, ldc=260) == INVALID    # BF16 C: pitch must be a multiple of 8 elements
+    assert _gemm(opB=0x400) == INVALID             # unknown flag bit
 
 
 def test_grouped_validation():
