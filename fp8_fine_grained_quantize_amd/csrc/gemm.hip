@@ -550,12 +550,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
   if (ILV) wait_vmcnt<0>();  // the last group's (empty) interleaved copies
 
   // ---- epilogue: four consecutive columns per lane, FP32 or (OB) BF16 ----
-  // The BF16 store derives the lane's row/column position afresh from the
-  // thread id (an opaque copy keeps the compiler from holding the loop-entry
-  // values in registers across the K loop, which made the 256x256 fold kernel
-  // spill inside the loop).
-  int tid_e = threadIdx.x;
-  if constexpr (OB) asm volatile("" : "+v"(tid_e));
+  const int tid_e = threadIdx.x;
   const int wm_e = (tid_e >> 6) / CFG::WAVES_N, wn_e = (tid_e >> 6) % CFG::WAVES_N;
   const int l16_e = tid_e & 15, lq_e = (tid_e >> 4) & 3;
   if constexpr (OB) {
