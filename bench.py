@@ -276,6 +276,8 @@ def main():
         # The step's GEMM with a BF16 output (the fused BF16 epilogue), over
         # the same rotating input sets, fold and power-of-two paths.
         Cb = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(S)]
+        Qo = [torch.empty(M, N, dtype=torch.uint8, device=dev) for _ in range(S)]
+        sQo = [torch.empty(N // 128, M, dtype=torch.float32, device=dev) for _ in range(S)]
         for p2 in (False, True):
             for j in range(S):
                 fb.quantize_1x128(A[j], pow2=p2, q=qA[j], s=sA[j])
@@ -285,7 +287,18 @@ def main():
             extras["fprop_gemm_bf16_out" + ("_pow2_scales" if p2 else "")] = {
                 "us": round(t * 1e3, 2), "TFLOP/s": round(flops / t / 1e9, 1),
                 "frac_mfma": round(flops / t / 1e9 / FP8_PEAK_TFLOPS, 4)}
-        del Cb
+            # quantize-on-store: the next layer's FP8 input (1x128, power-of-two
+            # scales) straight from the epilogue, against GEMM(BF16) + quantize_1x128
+            t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled_q1x128(
+                qA[i % S], sA[i % S], qW[i % S], sW[i % S], pow2_scales=p2, pow2=True, Q=Qo[i % S], sQ=sQo[i % S]), 40)
+            t2 = timed_events(torch, lambda i: (fb.gemm_fp8_blockscaled(qA[i % S], sA[i % S], qW[i % S], sW[i % S],
+                                                                        C=Cb[i % S], pow2_scales=p2),
+                                                fb.quantize_1x128(Cb[i % S], pow2=True, q=Qo[i % S], s=sQo[i % S])), 40)
+            extras["fprop_gemm_q1x128_pow2_out" + ("_pow2_scales" if p2 else "")] = {
+                "us": round(t * 1e3, 2), "TFLOP/s": round(flops / t / 1e9, 1),
+                "frac_mfma": round(flops / t / 1e9 / FP8_PEAK_TFLOPS, 4),
+                "unfused_bf16_gemm_plus_quantize_us": round(t2 * 1e3, 2)}
+        del Cb, Qo, sQo
         extras.update(run_extras(torch, fb, synthetic, dev, np))
 
     cpu = None

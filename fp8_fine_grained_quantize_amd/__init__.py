@@ -20,7 +20,7 @@ __all__ = [
     "Fp8BlkError", "lib", "library_path", "OP_N", "OP_T", "BSCALE_BLOCK128", "BSCALE_ROW128",
     "SCALE_POW2", "GEMM_POW2_SCALES", "GEMM_OUT_BF16", "quantize_1x128", "quantize_128x1", "quantize_block128",
     "requantize_128x1_from_1x128", "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled",
-    "quantize_128x1_grouped", "token_group_slots", "grouped_wgrad_fp8_blockscaled",
+    "quantize_128x1_grouped", "token_group_slots", "grouped_wgrad_fp8_blockscaled", "gemm_fp8_blockscaled_q1x128",
     "workspace_bytes", "status_string", "abi_version", "EXPORTED_SYMBOLS", "empty_pitched", "as_pitched",
 ]
 
@@ -41,6 +41,8 @@ _SIGNATURES = {
     "fp8blk_requantize_128x1_from_1x128": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _u32, _vp]),
     "fp8blk_gemm_fp8_blockscaled": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _vp, _int,
                                            _vp, _i64, _vp, _sz, _vp]),
+    "fp8blk_gemm_fp8_blockscaled_q1x128": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _vp, _vp, _i64,
+                                                  _vp, _u32, _vp]),
     "fp8blk_grouped_gemm_fp8_blockscaled": (_int, [_i64, _vp, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp,
                                                    _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "fp8blk_quantize_128x1_grouped": (_int, [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _u32, _vp]),
@@ -231,6 +233,21 @@ def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCAL
                                              _ptr(C), _pitch(C), ws_ptr, ws_bytes, _stream()),
            "gemm_fp8_blockscaled")
     return C
+
+
+def gemm_fp8_blockscaled_q1x128(A, sA, B, sB, opB: int = OP_N, pow2_scales: bool = False, pow2: bool = False,
+                                Q=None, sQ=None):
+    """Block-scaled GEMM (block-scaled B) whose output is quantized on store:
+    returns (Q uint8 [M][N], sQ float32 [ceil(N/128)][M]) = quantize_1x128 of
+    the BF16-rounded product, with power-of-two scales when pow2."""
+    M, K = A.shape
+    N = B.shape[1] if opB == OP_N else B.shape[0]
+    Q = _empty_pitched(M, N, torch.uint8, A.device, 1) if Q is None else Q
+    sQ = torch.empty((N + 127) // 128, M, dtype=torch.float32, device=A.device) if sQ is None else sQ
+    _check(lib().fp8blk_gemm_fp8_blockscaled_q1x128(
+        M, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), _pitch(B), opB | (GEMM_POW2_SCALES if pow2_scales else 0),
+        _ptr(sB), _ptr(Q), _pitch(Q), _ptr(sQ), SCALE_POW2 if pow2 else 0, _stream()), "gemm_fp8_blockscaled_q1x128")
+    return Q, sQ
 
 
 def grouped_gemm_fp8_blockscaled(offsets, A, sA, B, sB, opB: int = OP_N, max_group_rows=None, C=None,

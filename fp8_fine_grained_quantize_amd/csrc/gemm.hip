@@ -175,9 +175,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Row `row` of an output matrix of FP32 or BF16 elements.
-__device__ __forceinline__ void* out_row(void* C, int64_t ldc, int64_t row, bool bf16) {
-  return static_cast<char*>(C) + row * ldc * (bf16 ? 2 : 4);
+// Output modes of a GEMM kernel: FP32 C, BF16 C, or C quantized on store to
+// E4M3 with 1x128 scales (default or power-of-two scales).
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_Q_POW2 = 3 };
+constexpr int out_elem_bytes(int om) { return om == OUT_F32 ? 4 : om == OUT_BF16 ? 2 : 1; }
+
+// Row `row` of an output matrix whose elements have `esize` bytes.
+__device__ __forceinline__ void* out_row(void* C, int64_t ldc, int64_t row, int esize) {
+  return static_cast<char*>(C) + row * ldc * esize;
 }
 
 // Arguments of one output tile: where its operands start and how far they
@@ -193,8 +198,11 @@ struct TileArgs {
   int64_t n0, N;
   const float* sB;    // scale table of this B
   int64_t sB_ld;      // row length of the scale table
-  void* C;            // row m0 of C (FP32, or BF16 for the OB kernels)
+  void* C;            // row m0 of C (FP32, BF16 or E4M3 codes by the kernel's output mode)
   int64_t ldc;        // row pitch of C in elements
+  float* sQ;          // quantized output: its 1x128 scales [ceil(N/128)][sQ_ld]
+  int64_t sQ_ld;      //   (row count of the whole output)
+  int64_t m0;         //   first output row of this tile
   int64_t K;
   int g0, g1;         // K groups [g0, g1) of this tile's (partial) product
 };
@@ -371,11 +379,31 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
   const uint8_t* Bs = ops + CFG::A_BYTES;
 
   // Row scales of this lane's TM row tiles (contiguous by the copy plan).
+  // With TM = 8 the two 16-byte halves are read in an order alternating with
+  // bit 4 of the lane, so that the 32 lanes of each half-wave read 32
+  // distinct 16-byte slots (all four 16-lane groups need the same scales);
+  // the lane index is taken from an opaque copy of the thread id, so the
+  // address is formed per group instead of held in a register.
   float sa[TM];
+  if constexpr (TM % 8 == 0) {
+    int tid_s = tid;
+    asm volatile("" : "+v"(tid_s));
+    const int flip = (tid_s >> 4) & 1;
+    const float* srow = sc + wm * CFG::WTM + (tid_s & 15) * TM;
 #pragma unroll
-  for (int i = 0; i < TM; i += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
-    sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+    for (int i = 0; i < TM; i += 8) {
+      const float4 v0 = *reinterpret_cast<const float4*>(srow + i + 4 * flip);
+      const float4 v1 = *reinterpret_cast<const float4*>(srow + i + 4 * (flip ^ 1));
+      const float4 lo = flip ? v1 : v0, hi = flip ? v0 : v1;
+      sa[i] = lo.x; sa[i + 1] = lo.y; sa[i + 2] = lo.z; sa[i + 3] = lo.w;
+      sa[i + 4] = hi.x; sa[i + 5] = hi.y; sa[i + 6] = hi.z; sa[i + 7] = hi.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
+      sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+    }
   }
   // Column scales: one block value per wave, or four per column tile.
   float4 sbv[TN];
@@ -510,7 +538,7 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
 // LDS arrays (the two pipeline stages); the loop is unrolled by two so that
 // every access names its array at compile time, which lets the compiler see
 // that reading one stage does not have to wait for copies into the other.
-template <class CFG, bool OPB_T, bool ROW128, bool P2, bool OB>
+template <class CFG, bool OPB_T, bool ROW128, bool P2, int OM>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint8_t* ops1, float* sc0, float* sc1) {
   constexpr int TM = CFG::TM, TN = CFG::TN;
   const int g0 = t.g0, G = t.g1;
@@ -553,7 +581,69 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
   const int tid_e = threadIdx.x;
   const int wm_e = (tid_e >> 6) / CFG::WAVES_N, wn_e = (tid_e >> 6) % CFG::WAVES_N;
   const int l16_e = tid_e & 15, lq_e = (tid_e >> 4) & 3;
-  if constexpr (OB) {
+  if constexpr (OM == OUT_Q || OM == OUT_Q_POW2) {
+    // Quantize on store: the BF16-rounded results in 1x128 tiles along each
+    // row (a 128-column group is the columns of waves wn and wn^1), exactly
+    // as quantize_1x128 quantizes a BF16 matrix.
+    static_assert(CFG::WTN == 64 && CFG::WAVES_N % 2 == 0, "a 128-column scale group spans two waves");
+    constexpr bool QP2 = OM == OUT_Q_POW2;
+    const int wave_e = tid_e >> 6;
+    // Per row: max |BF16 bits| over this wave's columns < N, combined with
+    // the partner wave's through LDS (the stage buffer is free once every
+    // wave has left the K loop).
+    uint32_t* red = reinterpret_cast<uint32_t*>(ops0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = t.n0 + wn_e * CFG::WTN + 16 * j + 4 * lq_e;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (col + r < t.N) m = max(m, bf16_rne(acc[i][j][r]) & 0x7FFFu);
+      }
+      m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+      if (lq_e == 0) red[wave_e * CFG::WTM + 16 * i + l16_e] = m;
+    }
+    __syncthreads();
+    uint8_t* Q = static_cast<uint8_t*>(t.C);
+    const int64_t gcol = t.n0 + wn_e * CFG::WTN;  // first column of this wave
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
+      if (row >= t.rows) continue;
+      const uint32_t amax = max(red[wave_e * CFG::WTM + 16 * i + l16_e], red[(wave_e ^ 1) * CFG::WTM + 16 * i + l16_e]);
+      const TileScale ts = make_scale<QP2, true>(amax << 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = gcol + 16 * j + 4 * lq_e;
+        float y[4], xv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          xv[r] = __uint_as_float(bf16_rne(acc[i][j][r]) << 16);
+          y[r] = quotient_fast<QP2, true>(xv[r], ts);
+        }
+        if (__builtin_expect(ts.slow, 0)) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = quotient_slow(xv[r], ts.s);
+        }
+        const uint32_t codes = pack4_e4m3(y[0], y[1], y[2], y[3]);
+        uint8_t* dst = Q + row * t.ldc + col;
+        if (col + 3 < t.N) {
+          *reinterpret_cast<uint32_t*>(dst) = codes;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col + r < t.N) dst[r] = (uint8_t)(codes >> (8 * r));
+        }
+      }
+      if ((wn_e & 1) == 0 && lq_e == 0 && gcol < t.N) t.sQ[(gcol / 128) * t.sQ_ld + t.m0 + row] = ts.s;
+    }
+    return;
+  }
+  if constexpr (OM == OUT_BF16) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
@@ -621,21 +711,22 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nblocks, int64_t ti
   tn = in / gm;
 }
 
-template <class CFG, bool OPB_T, bool ROW128, bool P2, bool OB>
+template <class CFG, bool OPB_T, bool ROW128, bool P2, int OM>
 __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
                                                    int64_t lda, const float* __restrict__ sA,
                                                    const uint8_t* __restrict__ B, int64_t ldb,
                                                    const float* __restrict__ sB, int64_t sB_ld,
                                                    void* __restrict__ C, int64_t ldc, int64_t tiles_m,
-                                                   int64_t tiles_n, float* __restrict__ partials, int groups_per_split) {
+                                                   int64_t tiles_n, float* __restrict__ partials, int groups_per_split,
+                                                   float* __restrict__ sQ) {
   FP8BLK_DECLARE_STAGES(CFG);
   int64_t tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   // Split K: workgroup row blockIdx.y computes the partial product of K
   // groups [y*groups_per_split, ...) into its own [M][N] slice of `partials`.
   const int G = (int)(K / 128);
-  // (OB kernels are never split: a split GEMM writes FP32 partials and the
-  // reduction writes BF16.)
+  // (Only FP32-output kernels are split: a split GEMM writes FP32 partials
+  // and the reduction writes BF16 when asked to.)
   const int split = blockIdx.y;
   if (gridDim.y > 1) {
     C = partials + (int64_t)split * M * N;
@@ -654,12 +745,15 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
   t.N = N;
   t.sB = sB;
   t.sB_ld = sB_ld;
-  t.C = out_row(C, ldc, m0, OB);
+  t.C = out_row(C, ldc, m0, out_elem_bytes(OM));
   t.ldc = ldc;
+  t.sQ = sQ;
+  t.sQ_ld = M;
+  t.m0 = m0;
   t.K = K;
   t.g0 = split * groups_per_split;
   t.g1 = t.g0 + groups_per_split < G ? t.g0 + groups_per_split : G;
-  gemm_tile<CFG, OPB_T, ROW128, P2, OB>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, OPB_T, ROW128, P2, OM>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Grouped: tiles are enumerated expert by expert, within an expert column
@@ -667,7 +761,7 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
 // workgroups share each expert's weight tile.  The per-expert row counts are
 // read from the device-resident offsets (prefix scan in LDS), so the host
 // never synchronizes; surplus workgroups of the upper-bound grid exit.
-template <class CFG, bool OPB_T, bool P2, bool OB>
+template <class CFG, bool OPB_T, bool P2, int OM>
 __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32_t* __restrict__ offsets,
                                                            int64_t M_total, int64_t N, int64_t K,
                                                            const uint8_t* __restrict__ A, int64_t lda,
@@ -739,12 +833,12 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   t.N = N;
   t.sB = sB + e * stride_sB;
   t.sB_ld = sB_ld;
-  t.C = out_row(C, ldc, m0, OB);
+  t.C = out_row(C, ldc, m0, out_elem_bytes(OM));
   t.ldc = ldc;
   t.K = K;
   t.g0 = 0;
   t.g1 = (int)(K / 128);
-  gemm_tile<CFG, OPB_T, false, P2, OB>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, OPB_T, false, P2, OM>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Grouped Wgrad of MoE experts: dW_e = X_e^T dY_e for every expert e, both
@@ -754,7 +848,7 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
 // Every expert's output has the same M x N tiles; tiles are enumerated expert
 // by expert, column tile by column tile, row tiles innermost.  An expert
 // without tokens gets dW_e = 0.
-template <class CFG, bool P2, bool OB>
+template <class CFG, bool P2, int OM>
 __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __restrict__ offsets, int64_t M, int64_t N,
                                                             const uint8_t* __restrict__ A, int64_t lda,
                                                             const float* __restrict__ sA,
@@ -783,12 +877,12 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __rest
   t.N = N;
   t.sB = sB;
   t.sB_ld = N;
-  t.C = out_row(out_row(C, strideC, e, OB), ldc, m0, OB);
+  t.C = out_row(out_row(C, strideC, e, out_elem_bytes(OM)), ldc, m0, out_elem_bytes(OM));
   t.ldc = ldc;
   t.K = 128 * (pg + ng);
   t.g0 = (int)pg;
   t.g1 = (int)(pg + ng);
-  gemm_tile<CFG, true, true, P2, OB>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, true, true, P2, OM>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Split-K reduction: C[m][n] = sum over s = 0 .. S-1, in that order, of the
@@ -863,11 +957,12 @@ static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8
   const int64_t per = ceil_div(G, S);
   S = ceil_div(G, per);  // no empty split
   if (out_bf16 && S == 1)
-    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2, true>), dim3((unsigned)blocks), dim3(CFG::NT), 0, stream, M, N,
-                       K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per);
+    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2, OUT_BF16>), dim3((unsigned)blocks), dim3(CFG::NT), 0, stream, M,
+                       N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per, nullptr);
   else
-    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2, false>), dim3((unsigned)blocks, (unsigned)S), dim3(CFG::NT), 0,
-                       stream, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per);
+    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, ROW128, P2, OUT_F32>), dim3((unsigned)blocks, (unsigned)S), dim3(CFG::NT), 0,
+                       stream, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, tiles_m, tiles_n, partials, (int)per,
+                       nullptr);
   if (S > 1) {
     if (hipGetLastError() != hipSuccess) return FP8BLK_ERR_LAUNCH;
     const int64_t chunks = M * ceil_div(N, 4);
@@ -957,6 +1052,62 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
   return dispatch_dense<SmallCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
 }
 
+// Dense GEMM with the output quantized on store (1x128 tiles along each row
+// of the BF16-rounded result); block-scaled B only, never split.
+template <class CFG, bool OPB_T, bool P2>
+static fp8blk_status_t launch_q(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
+                                const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_ld, uint8_t* Q, int64_t ldq,
+                                float* sQ, bool qpow2, hipStream_t st) {
+  const int64_t tiles_m = ceil_div(M, CFG::BM), tiles_n = ceil_div(N, CFG::BN);
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
+  const int per = (int)(K / 128);
+  if (qpow2)
+    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, false, P2, OUT_Q_POW2>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, M, N,
+                       K, A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, tiles_m, tiles_n, nullptr, per, sQ);
+  else
+    hipLaunchKernelGGL((k_gemm<CFG, OPB_T, false, P2, OUT_Q>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, M, N, K,
+                       A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, tiles_m, tiles_n, nullptr, per, sQ);
+  return launch_status();
+}
+
+template <class CFG>
+static fp8blk_status_t dispatch_q(bool t, bool p2, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                  const float* sA, const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_ld,
+                                  uint8_t* Q, int64_t ldq, float* sQ, bool qpow2, hipStream_t st) {
+  if (p2) {
+    if (t) return launch_q<CFG, true, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, sQ, qpow2, st);
+    return launch_q<CFG, false, true>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, sQ, qpow2, st);
+  }
+  if (t) return launch_q<CFG, true, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, sQ, qpow2, st);
+  return launch_q<CFG, false, false>(M, N, K, A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, sQ, qpow2, st);
+}
+
+extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled_q1x128(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                                              int64_t lda, const float* sA, const uint8_t* B,
+                                                              int64_t ldb, int opB, const float* sB, uint8_t* Q,
+                                                              int64_t ldq, float* sQ, uint32_t qflags, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8BLK_ERR_INVALID_ARG;
+  if (qflags & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
+  const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
+  opB &= ~FP8BLK_GEMM_POW2_SCALES;
+  if (opB != FP8BLK_OP_N && opB != FP8BLK_OP_T) return FP8BLK_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP8BLK_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP8BLK_OK;
+  if (K == 0) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(A, M, K, lda, 1) || !matrix_ok(Q, M, N, ldq, 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (opB == FP8BLK_OP_N ? !matrix_ok(B, K, N, ldb, 1) : !matrix_ok(B, N, K, ldb, 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (lda >= kMaxPitch || ldb >= kMaxPitch) return FP8BLK_ERR_UNSUPPORTED;
+  const int64_t G = K / 128, NB = ceil_div(N, 128);
+  if (!vec_ok(sA, G * M) || !vec_ok(sB, G * NB) || !vec_ok(sQ, NB * M)) return FP8BLK_ERR_INVALID_ARG;
+  const int64_t sB_ld = opB == FP8BLK_OP_N ? NB : G;
+  const bool t = opB == FP8BLK_OP_T, qpow2 = (qflags & FP8BLK_SCALE_POW2) != 0;
+  hipStream_t st = as_stream(stream);
+  const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
+  if (big_tiles >= 128) return dispatch_q<BigCfg>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, sQ, qpow2, st);
+  return dispatch_q<SmallCfg>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, Q, ldq, sQ, qpow2, st);
+}
+
 extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
     int64_t G, const int32_t* group_offsets, int64_t M_total, int64_t max_group_rows, int64_t N, int64_t K,
     const uint8_t* A, int64_t lda, const float* sA, const uint8_t* B, int64_t ldb, int64_t strideB, int opB,
@@ -1001,7 +1152,7 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   hipLaunchKernelGGL((k_grouped_gemm<CFG, T_, P2_, OB_>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, G,          \
                      group_offsets, M_total, N, K, A, lda, sA, B, ldb, strideB, sB, stride_sB, sB_ld, C, ldc, tiles_n)
 #define FP8BLK_GROUPED_LAUNCH_OB(T_, P2_) \
-  if (ob) FP8BLK_GROUPED_LAUNCH(T_, P2_, true); else FP8BLK_GROUPED_LAUNCH(T_, P2_, false)
+  if (ob) FP8BLK_GROUPED_LAUNCH(T_, P2_, OUT_BF16); else FP8BLK_GROUPED_LAUNCH(T_, P2_, OUT_F32)
   if (opB == FP8BLK_OP_T) {
     if (p2) { FP8BLK_GROUPED_LAUNCH_OB(true, true); } else { FP8BLK_GROUPED_LAUNCH_OB(true, false); }
   } else {
@@ -1044,9 +1195,9 @@ extern "C" fp8blk_status_t fp8blk_grouped_wgrad_fp8_blockscaled(int64_t G, const
   hipLaunchKernelGGL((k_grouped_wgrad<CFG, P2_, OB_>), dim3((unsigned)blocks), dim3(CFG::NT), 0, st, group_offsets, M, \
                      N, AT, ldaT, sA, BT, ldbT, sB, C, ldc, strideC, tiles_m, tiles_n)
   if (p2) {
-    if (ob) FP8BLK_WGRAD_LAUNCH(true, true); else FP8BLK_WGRAD_LAUNCH(true, false);
+    if (ob) FP8BLK_WGRAD_LAUNCH(true, OUT_BF16); else FP8BLK_WGRAD_LAUNCH(true, OUT_F32);
   } else {
-    if (ob) FP8BLK_WGRAD_LAUNCH(false, true); else FP8BLK_WGRAD_LAUNCH(false, false);
+    if (ob) FP8BLK_WGRAD_LAUNCH(false, OUT_BF16); else FP8BLK_WGRAD_LAUNCH(false, OUT_F32);
   }
 #undef FP8BLK_WGRAD_LAUNCH
   return launch_status();

@@ -186,6 +186,24 @@ fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                             void* stream);
 
 /*
+ * The same GEMM with its output quantized on store for the next layer's
+ * input (the pages quantize activations to FP8 before the next FP8 GEMM
+ * and keep such caches in FP8 [p2¶4; p5¶4]): with C the FP32 result
+ * defined above,
+ *   (Q, sQ) = fp8blk_quantize_1x128 applied to C rounded to BF16 (nearest
+ *             even), with flags qflags (0 or FP8BLK_SCALE_POW2),
+ * computed in the GEMM's epilogue without writing C.
+ *   Q   [M][N] E4M3 codes, pitch ldq >= N; sQ [ceil(N/128)][M] FP32.
+ *   B is block-scaled (FP8BLK_BSCALE_BLOCK128 layouts); opB as above,
+ *   FP8BLK_GEMM_POW2_SCALES allowed; K a positive multiple of 128; never
+ *   split along K.
+ */
+fp8blk_status_t fp8blk_gemm_fp8_blockscaled_q1x128(int64_t M, int64_t N, int64_t K,
+                                                   const uint8_t* A, int64_t lda, const float* sA,
+                                                   const uint8_t* B, int64_t ldb, int opB,
+                                                   const float* sB, uint8_t* Q, int64_t ldq,
+                                                   float* sQ, uint32_t qflags, void* stream);
+/*
  * Grouped (per-expert) block-scaled FP8 GEMM for MoE expert projections
  * [p2¶4]: for each expert e,
  *   C[off[e]:off[e+1]][:] = A[off[e]:off[e+1]][:] * B_e
@@ -279,7 +297,8 @@ size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
 /* Human-readable name of a status code (static string). */
 const char* fp8blk_status_string(fp8blk_status_t status);
 
-/* ABI version of this header: 2 (2 added the MoE backward entry points). */
+/* ABI version of this header: 3 (2 added the MoE backward entry points, 3 the
+ * BF16 output flag and the quantize-on-store GEMM). */
 int fp8blk_abi_version(void);
 
 #ifdef __cplusplus

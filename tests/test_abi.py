@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fb.abi_version() == 2
+    assert fb.abi_version() == 3
     assert fb.token_group_slots(65536, 256) == 512 + 256
     assert fb.token_group_slots(100, 3) == 3 and fb.token_group_slots(-1, 3) == 0
     assert fb.status_string(0) == "FP8BLK_OK"
@@ -118,6 +118,21 @@ def test_gemm_validation():
     assert _gemm(M=0) == OK and _gemm(N=0) == OK
     assert _gemm(opB=0x200, ldc=260) == INVALID    # BF16 C: pitch must be a multiple of 8 elements
     assert _gemm(opB=0x400) == INVALID             # unknown flag bit
+
+
+def test_q1x128_validation():
+    f = fb.lib().fp8blk_gemm_fp8_blockscaled_q1x128
+
+    def call(M=256, N=256, K=256, A=FAKE, lda=256, sA=FAKE, B=FAKE, ldb=256, opB=0, sB=FAKE, Q=FAKE, ldq=256,
+             sQ=FAKE, qflags=0):
+        return f(M, N, K, A, lda, sA, B, ldb, opB, sB, Q, ldq, sQ, qflags, NULL)
+
+    assert call(Q=NULL) == INVALID and call(sQ=NULL) == INVALID
+    assert call(ldq=200) == INVALID             # below N
+    assert call(ldq=264) == INVALID             # not a 16-byte multiple
+    assert call(qflags=2) == INVALID
+    assert call(K=200) == INVALID and call(opB=2) == INVALID
+    assert call(M=0) == OK and call(N=0) == OK
 
 
 def test_grouped_validation():
