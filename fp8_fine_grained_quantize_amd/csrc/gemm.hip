@@ -175,6 +175,22 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// 4 x 4 transpose between the four 16-lane rows of a wave and four
+// registers: afterwards register k of lane l16 + 16 r holds what register r
+// of lane l16 + 16 k held.  Two swaps of wave halves (v_permlane32_swap),
+// then two swaps of neighbouring rows (v_permlane16_swap).  Every lane of the
+// wave must be active.
+__device__ __forceinline__ void transpose_rows4(uint32_t (&c)[4]) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
+  const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  c[0] = s01[0];
+  c[1] = s01[1];
+  c[2] = s23[0];
+  c[3] = s23[1];
+}
+
 // Output modes of a GEMM kernel: FP32 C, BF16 C, or C quantized on store to
 // E4M3 with 1x128 scales (default or power-of-two scales).
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_Q_POW2 = 3 };
@@ -246,7 +262,13 @@ struct CopyPlan {
   // Per-lane byte offset of this lane's scale copy, recomputed at each issue
   // from an opaque copy of the thread id: a few integer operations per group,
   // one VGPR less held across the K loop (the 256x256 fold kernels run at
-  // the register limit).
+  // the register limit).  SEL: both offsets are formed and one is selected.
+  // Copies issued from inside a row loop need that: there a branch would
+  // split the loop into two blocks, and the compiler then sinks every MFMA
+  // of the group below it, past the scheduling fences.  The copies issued at
+  // the group start keep the branch, which leaves the BF16-output fold
+  // kernel one register short of a spill.
+  template <bool SEL>
   __device__ __forceinline__ uint32_t sc_offset(const TileArgs& t) const {
     constexpr int TM = CFG::TM, WTM = CFG::WTM;
     int tid = threadIdx.x;
@@ -257,14 +279,15 @@ struct CopyPlan {
     const int p = blk * 64 + lane;      // float position in the [BM + BN] scale buffer
     // BM is a multiple of 64, so the row/column choice is uniform per wave
     // (derived from blk alone), which keeps the resource in scalar registers.
-    if (blk * 64 < BM) {
-      const int w = p / WTM, q = p % WTM;
-      return (uint32_t)((w * WTM + 16 * (q % TM) + q / TM) * 4);
-    }
-    if (ROW128) return (uint32_t)((p - BM) * 4);  // column scale of column n0 + (p - BM)
-    // block scale of column block n0/128 + (p - BM); only the first BN/128
-    // positions are used
-    return (uint32_t)((p - BM) * (OPB_T ? t.K / 128 : 1) * 4);
+    const int w = p / WTM, q = p % WTM;
+    const uint32_t row_off = (uint32_t)((w * WTM + 16 * (q % TM) + q / TM) * 4);
+    // column scale of column n0 + (p - BM), or block scale of column block
+    // n0/128 + (p - BM) (only the first BN/128 positions are used)
+    const uint32_t col_off =
+        ROW128 ? (uint32_t)((p - BM) * 4) : (uint32_t)((p - BM) * (OPB_T ? (int)(t.K >> 7) : 1) * 4);
+    if constexpr (SEL) return blk * 64 < BM ? row_off : col_off;
+    if (blk * 64 < BM) return row_off;
+    return col_off;
   }
 
   __device__ __forceinline__ void issue(const TileArgs& t, int g, uint8_t* buf, float* sbuf) const {
@@ -301,6 +324,7 @@ struct CopyPlan {
   // Copy number n (0 .. LOADS-1) of a group: A blocks, then B blocks, then
   // the scale block.
   static constexpr int LOADS = CFG::A_ITERS + CFG::B_ITERS + 1;
+  template <bool SEL = false>
   __device__ __forceinline__ void issue_one(v4i ra, v4i rb,
                                             v4i rsa, v4i rsb, int n,
                                             const TileArgs& t, uint8_t* buf, float* sbuf) const {
@@ -316,7 +340,7 @@ struct CopyPlan {
       const int blk = wave < CFG::S_BLOCKS ? wave : 0;
       const bool rows = blk * 64 < BM;  // wave-uniform; a select keeps the copy branch-free
       const v4i rs = v4i{rows ? rsa[0] : rsb[0], rows ? rsa[1] : rsb[1], rows ? rsa[2] : rsb[2], rows ? rsa[3] : rsb[3]};
-      dma4(rs, sc_offset(t), (uint8_t*)(sbuf + blk * 64));
+      dma4(rs, sc_offset<SEL>(t), (uint8_t*)(sbuf + blk * 64));
     }
   }
 };
@@ -364,7 +388,11 @@ __device__ __forceinline__ v4f mfma_e8m0_sel(int oa, int ob, const v8i& a, const
 // E8M0 code of a power-of-two FP32 scale: its biased exponent.
 __device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
 
-template <class CFG, bool OPB_T, bool ROW128, bool P2>
+// LEAN_SC: form the row-scale addresses per group from an opaque copy of the
+// thread id (fewer live registers across the K loop, at a small cost in
+// issue); the kernels whose epilogue quantizes on store need it to stay
+// free of spills.
+template <class CFG, bool OPB_T, bool ROW128, bool P2, bool LEAN_SC = false>
 __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
                                               v4f (&acc)[CFG::TM][CFG::TN],
                                               const CopyPlan<CFG, OPB_T, ROW128>& plan, const TileArgs& t, int gnext,
@@ -379,13 +407,12 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
   const uint8_t* Bs = ops + CFG::A_BYTES;
 
   // Row scales of this lane's TM row tiles (contiguous by the copy plan).
-  // With TM = 8 the two 16-byte halves are read in an order alternating with
-  // bit 4 of the lane, so that the 32 lanes of each half-wave read 32
-  // distinct 16-byte slots (all four 16-lane groups need the same scales);
-  // the lane index is taken from an opaque copy of the thread id, so the
-  // address is formed per group instead of held in a register.
   float sa[TM];
-  if constexpr (TM % 8 == 0) {
+  if constexpr (LEAN_SC && TM % 8 == 0) {
+    // The two 16-byte halves are read in an order alternating with bit 4 of
+    // the lane, so that the 32 lanes of each half-wave read 32 distinct
+    // 16-byte slots (all four 16-lane groups need the same scales).  This
+    // form measured 2-3% slower in the kernels that do not need it.
     int tid_s = tid;
     asm volatile("" : "+v"(tid_s));
     const int flip = (tid_s >> 4) & 1;
@@ -489,7 +516,7 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
       if constexpr (ILV) {
 #pragma unroll
         for (int n = (i * LOADS) / TM; n < ((i + 1) * LOADS) / TM; ++n)
-          plan.issue_one(cr.a, cr.b, cr.sa, cr.sb, n, t, nbuf, nsbuf);
+          plan.template issue_one<true>(cr.a, cr.b, cr.sa, cr.sb, n, t, nbuf, nsbuf);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -563,14 +590,14 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     __syncthreads();
     if (!ILV && g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_group<CFG, OPB_T, ROW128, P2>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
+    compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q)>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
     if (g + 1 < G) {
       wait_vmcnt<0>();
       __syncthreads();
       if (!ILV && g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group<CFG, OPB_T, ROW128, P2>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
+      compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q)>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -608,17 +635,21 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
       if (lq_e == 0) red[wave_e * CFG::WTM + 16 * i + l16_e] = m;
     }
     __syncthreads();
+    // The codes of a row tile are transposed across the wave's four 16-lane
+    // rows, so that lane (l16, lq) stores columns 16 lq .. 16 lq + 15 of the
+    // wave's 64 as one 16-byte word (4x fewer, 4x wider stores).
+    static_assert(TN == 4, "the store transpose covers four column tiles");
     uint8_t* Q = static_cast<uint8_t*>(t.C);
     const int64_t gcol = t.n0 + wn_e * CFG::WTN;  // first column of this wave
+    const int64_t qcol = gcol + 16 * lq_e;        // first column this lane stores
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
-      if (row >= t.rows) continue;
       const uint32_t amax = max(red[wave_e * CFG::WTM + 16 * i + l16_e], red[(wave_e ^ 1) * CFG::WTM + 16 * i + l16_e]);
       const TileScale ts = make_scale<QP2, true>(amax << 16);
+      uint32_t codes[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int64_t col = gcol + 16 * j + 4 * lq_e;
         float y[4], xv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -629,38 +660,49 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = quotient_slow(xv[r], ts.s);
         }
-        const uint32_t codes = pack4_e4m3(y[0], y[1], y[2], y[3]);
-        uint8_t* dst = Q + row * t.ldc + col;
-        if (col + 3 < t.N) {
-          *reinterpret_cast<uint32_t*>(dst) = codes;
-        } else {
+        codes[j] = pack4_e4m3(y[0], y[1], y[2], y[3]);
+      }
+      transpose_rows4(codes);
+      if (row >= t.rows) continue;
+      uint8_t* dst = Q + row * t.ldc + qcol;
+      if (qcol + 15 < t.N) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+      } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (col + r < t.N) dst[r] = (uint8_t)(codes >> (8 * r));
-        }
+        for (int b = 0; b < 16; ++b)
+          if (qcol + b < t.N) dst[b] = (uint8_t)(codes[b >> 2] >> (8 * (b & 3)));
       }
       if ((wn_e & 1) == 0 && lq_e == 0 && gcol < t.N) t.sQ[(gcol / 128) * t.sQ_ld + t.m0 + row] = ts.s;
     }
     return;
   }
   if constexpr (OM == OUT_BF16) {
+    // BF16 pairs transposed across the wave's 16-lane rows as for the
+    // quantized output: lane (l16, lq) stores columns 16 lq .. 16 lq + 15 of
+    // the wave's 64 as two 16-byte words.
+    static_assert(TN == 4, "the store transpose covers four column tiles");
+    const int64_t qcol = t.n0 + wn_e * CFG::WTN + 16 * lq_e;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
-      if (row >= t.rows) continue;
+      uint32_t lo[TN], hi[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int64_t col = t.n0 + wn_e * CFG::WTN + 16 * j + 4 * lq_e;
-        uint16_t* dst = static_cast<uint16_t*>(t.C) + row * t.ldc + col;
-        const uint32_t b0 = bf16_rne(acc[i][j][0]), b1 = bf16_rne(acc[i][j][1]);
-        const uint32_t b2 = bf16_rne(acc[i][j][2]), b3 = bf16_rne(acc[i][j][3]);
-        if (col + 3 < t.N) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        } else {
-          const uint32_t b[4] = {b0, b1, b2, b3};
+        lo[j] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        hi[j] = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+      }
+      transpose_rows4(lo);
+      transpose_rows4(hi);
+      if (row >= t.rows) continue;
+      uint16_t* dst = static_cast<uint16_t*>(t.C) + row * t.ldc + qcol;
+      if (qcol + 15 < t.N) {
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+        reinterpret_cast<uint4*>(dst)[1] = make_uint4(lo[2], hi[2], lo[3], hi[3]);
+      } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (col + r < t.N) dst[r] = (uint16_t)b[r];
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t w = (e & 2) ? hi[e >> 2] : lo[e >> 2];
+          if (qcol + e < t.N) dst[e] = (uint16_t)(w >> (16 * (e & 1)));
         }
       }
     }
