@@ -445,3 +445,86 @@ def gemm_unquantized(A_bits: np.ndarray, B_bits: np.ndarray, opB: int = OP_N) ->
     if opB == OP_T:
         B = B.T
     return A @ B
+
+
+# --------------------------------------------------------------------------
+# Context only: limited-precision accumulation of FP8 products
+# --------------------------------------------------------------------------
+#
+# The pages report that the H800 tensor core adds FP8 products in fixed
+# point, aligning them to the largest exponent by right shifts before the
+# addition [p5¶4], that the sum keeps only about 14 bits [p2¶3], and that
+# over K = 4096 this gives a maximum relative error of nearly 2 % [p2¶2].
+# They say neither how many products are aligned together nor whether the
+# shifted-out bits are truncated or rounded.  Readings taken here: each step
+# adds `width` products and the running accumulator; every one of those
+# terms is truncated toward zero (a right shift of a sign-magnitude
+# mantissa) to a multiple of 2^(E - bits), where 2^(E-1) <= the largest
+# |term| < 2^E; the exact sum of the truncated terms becomes the new FP32
+# accumulator.  This models no kernel of this library (the gfx950 MFMA is not
+# emulated here); it is context for the accumulation study, and whether it
+# matches the H800 is unpinned.
+
+
+def limited_dot(a: np.ndarray, b: np.ndarray, width: int = 32, bits: int = 14) -> np.ndarray:
+    """sum_k a[..., k] * b[..., k] accumulated as described above, in steps
+    of `width` products along the last axis (a and b broadcast; their values
+    are exact FP8 values, so every product is exact in FP64).  Returns
+    float64 holding FP32 values."""
+    assert bits + int(np.ceil(np.log2(width + 1))) <= 53, "truncated terms must sum exactly in FP64"
+    K = a.shape[-1]
+    acc = np.zeros(np.broadcast_shapes(a.shape[:-1], b.shape[:-1]), np.float64)
+    for k0 in range(0, K, width):
+        prods = a[..., k0:k0 + width] * b[..., k0:k0 + width]
+        terms = np.concatenate([acc[..., None], prods], axis=-1)
+        _, ex = np.frexp(terms)  # |t| in [2^(ex-1), 2^ex) for t != 0
+        ex = np.where(terms != 0, ex, -(1 << 20))
+        emax = ex.max(axis=-1)
+        zero = emax == -(1 << 20)
+        lsb = np.ldexp(1.0, np.where(zero, 0, emax - bits))[..., None]
+        kept = np.trunc(terms / lsb) * lsb  # toward zero; exact (lsb is a power of two)
+        acc = kept.sum(axis=-1).astype(np.float32).astype(np.float64)
+    return acc
+
+
+def quantize_per_tensor(x_bits: np.ndarray):
+    """One scale for the whole tensor, s = fl32(amax / 448), codes
+    enc(fl32(x / s)): the tensor-wise scaling the pages contrast with their
+    tiles [p2¶2].  Returns (q uint8, s float32 scalar)."""
+    x = bf16_bits_to_f32(x_bits)
+    amax = np.array([np.max(np.abs(x)) if x.size else 0.0], np.float32)
+    s = tile_scale(amax, False)
+    return _encode_tiles(x, s[0]), s[0]
+
+
+def gemm_limited_per_tensor(A: np.ndarray, sA, B: np.ndarray, sB, width: int = 32, bits: int = 14) -> np.ndarray:
+    """C = sA * sB * (limited sum over all of K of dec(A[m,k]) * dec(B[k,n])):
+    tensor-wise scales and the whole K accumulated in the tensor core, the
+    setting of the pages' 2 % figure [p2¶2].  A [M][K], B [K][N] codes."""
+    Ad = e4m3_decode(A)
+    Bd = e4m3_decode(B)
+    P = limited_dot(Ad[:, None, :], Bd.T[None, :, :], width, bits)
+    return P * (np.float64(sA) * np.float64(sB))
+
+
+def gemm_blockscaled_limited(A: np.ndarray, sA: np.ndarray, B: np.ndarray, sB: np.ndarray,
+                             width: int = 32, bits: int = 14) -> np.ndarray:
+    """The pages' method on the H800 as they describe it: each 128-deep group
+    summed in the tensor core with limited accumulation (starting from zero),
+    then promoted to FP32 on the vector cores, multiplied by the group's
+    scales and added to an FP32 accumulator [p2¶3, p2¶4].  A [M][K] 1x128,
+    B [K][N] with 128x128 block scales (opB = N).  Returns float64 holding
+    FP32 values."""
+    M, K = A.shape
+    assert K % TILE == 0
+    Ad = e4m3_decode(A)
+    Bd = e4m3_decode(B)
+    N = Bd.shape[1]
+    C = np.zeros((M, N), np.float32)
+    for g in range(K // TILE):
+        ks = slice(g * TILE, (g + 1) * TILE)
+        P = limited_dot(Ad[:, None, ks], Bd[ks, :].T[None, :, :], width, bits).astype(np.float32)
+        S = (sA[g].astype(np.float32)[:, None] * _b_scale_for_group(sB, g, N, OP_N, BSCALE_BLOCK128)
+             .astype(np.float32)[None, :])
+        C = (C + P * S).astype(np.float32)
+    return C.astype(np.float64)
