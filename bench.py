@@ -16,7 +16,7 @@ MFMA peak.  `kernels` adds each kernel's time and roofline fraction (the
 quantizers from a second pass of the same steps with events between all
 kernels), and `extras` times the other workloads' kernels
 (backward Dgrad/Wgrad, the accumulation study, the MoE grouped GEMMs).
-`cpu_baseline` times the CPU oracle on a bounded sample of the step.
+`cpu_baseline` times the CPU oracle on the whole step, repeated for at least 10 s.
 
     python bench.py [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 """
@@ -372,11 +372,16 @@ def run_extras(torch, fb, synthetic, dev, np):
         t = timed_events(torch, lambda i: fn(x, q=qo, s=so) if fn is not fb.quantize_128x1 else fn(x, qT=qo, s=so), reps)
         gbs = x.numel() * bpe / (t * 1e-3) / 1e9
         res[name] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    qT2, sT2 = fb.requantize_128x1_from_1x128(qdY, sdY)
-    t = timed_events(torch, lambda i: fb.requantize_128x1_from_1x128(qdY, sdY, qT=qT2, sT=sT2), reps)
-    gbs = dY.numel() * (1 + 1 + 8 / 128) / (t * 1e-3) / 1e9
-    res["requantize_128x1_from_1x128_dY"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1),
-                                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    # the pages' backward path: the cached 1x128 FP8 copy re-quantized to
+    # 128x1, for dY and for the activations X (the cached forward input)
+    qX, sX = fb.quantize_1x128(Xd)
+    for name, qs, ss, n in [("requantize_128x1_from_1x128_dY", qdY, sdY, dY.numel()),
+                            ("requantize_128x1_from_1x128_X", qX, sX, X.numel())]:
+        qT2, sT2 = fb.requantize_128x1_from_1x128(qs, ss)
+        t = timed_events(torch, lambda i: fb.requantize_128x1_from_1x128(qs, ss, qT=qT2, sT=sT2), reps)
+        gbs = n * (1 + 1 + 8 / 128) / (t * 1e-3) / 1e9
+        res[name] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    del qX, sX, qT2, sT2
     del Xd, Wd, dYd, qXT, qdYT, Cd, Cw
     # accumulation study shapes
     for Kc in (4096, 8192, 16384):

@@ -75,7 +75,7 @@ __device__ __forceinline__ TileScale make_scale(uint32_t amax_bits) {
   }
   if (!POW2) {
     const float amax = __uint_as_float(amax_bits);
-    t.s = amax / kE4M3Max;  // IEEE division (fp32 division is correctly rounded in this build)
+    t.s = amax / kE4M3Max;  // IEEE division (the library is compiled with correctly rounded fp32 division)
     t.r = 1.0f / t.s;
     t.slow = !(FASTDIV && t.s >= 0x1p-100f && t.s <= 0x1p100f);
     return t;

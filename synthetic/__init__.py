@@ -30,6 +30,14 @@ cast):
                    gradient of its output), "dh" [rows][4096] ~N(0,1e-3) (the
                    gradient of the up projection's output); each from its own
                    generator seeded 3000/3001/3002 on the requested device.
+* ``large_bf16``   tensors past 2^31 elements for the index-range tests:
+                   BF16 ~N(0,1) drawn directly in BF16 by a device generator
+                   seeded by the caller, every 97th row scaled by 2^20 and
+                   every 89th by 2^-20 (the scale range).
+* ``random_codes`` / ``random_scales``  GEMM operands drawn directly: E4M3
+                   codes uniform over all 256 byte values with the two NaN
+                   codes replaced by 0x7E / 0xFE, and FP32 scales 2^u with u
+                   uniform in (-12, 0]; device generator seeded by the caller.
 
 The hidden size 7168, the expert count 256 with top-8 routing and the expert
 width 2048 follow the DeepSeek-V3 description (inprokorea.com wr_id 890463,
@@ -44,6 +52,7 @@ import torch
 __all__ = [
     "bf16_bits", "randn_bf16", "single_gemm", "dense_fprop", "accum_study",
     "moe_routing", "expert_weight", "backward", "edge_tensor", "moe_grad",
+    "large_bf16", "random_codes", "random_scales",
 ]
 
 
@@ -150,3 +159,24 @@ def edge_tensor(shape, seed: int, zero_tile_every: int = 7) -> torch.Tensor:
     if len(shape) == 2 and zero_tile_every:
         t[::zero_tile_every, :] = 0
     return t
+
+
+def large_bf16(shape, seed: int, device="cuda") -> torch.Tensor:
+    g = torch.Generator(device=device).manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
+    x[::97] *= 2.0 ** 20
+    x[::89] *= 2.0 ** -20
+    return x
+
+
+def random_codes(shape, seed: int, device="cuda") -> torch.Tensor:
+    g = torch.Generator(device=device).manual_seed(seed)
+    c = torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.uint8)
+    nan = (c & 0x7F) == 0x7F
+    c[nan] -= 1
+    return c
+
+
+def random_scales(shape, seed: int, device="cuda") -> torch.Tensor:
+    g = torch.Generator(device=device).manual_seed(seed)
+    return torch.exp2(torch.rand(shape, generator=g, device=device) * -12.0)

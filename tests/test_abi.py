@@ -14,7 +14,7 @@ import fp8_fine_grained_quantize_amd as fb
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "libfp8blk.h")
 
-INVALID, OK = 1, 0
+INVALID, OK, UNSUPPORTED = 1, 0, 2
 
 
 def _declared():
@@ -118,6 +118,9 @@ def test_gemm_validation():
     assert _gemm(M=0) == OK and _gemm(N=0) == OK
     assert _gemm(opB=0x200, ldc=260) == INVALID    # BF16 C: pitch must be a multiple of 8 elements
     assert _gemm(opB=0x400) == INVALID             # unknown flag bit
+    # per-lane copy offsets are 32-bit: operand pitches of 2^23 bytes or more are refused
+    assert _gemm(lda=1 << 23) == UNSUPPORTED
+    assert _gemm(opB=1, ldb=1 << 23) == UNSUPPORTED
 
 
 def test_q1x128_validation():
