@@ -708,6 +708,23 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     }
     return;
   }
+  // FP32: four consecutive columns per lane as one 16-byte store.  Tiles
+  // wholly inside the matrix take a path with no per-lane column test: with
+  // the test and its element-wise tail in the same code, the compiler merged
+  // the two into four predicated 4-byte stores per tile column.
+  if (t.n0 + CFG::BN <= t.N && t.rows >= CFG::BM) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = t.n0 + wn_e * CFG::WTN + 16 * j + 4 * lq_e;
+        *reinterpret_cast<float4*>(static_cast<float*>(t.C) + row * t.ldc + col) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
