@@ -709,13 +709,16 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     return;
   }
   // FP32: four consecutive columns per lane as one 16-byte store.  Tiles
-  // wholly inside the matrix take a path with no per-lane column test: with
-  // the test and its element-wise tail in the same code, the compiler merged
-  // the two into four predicated 4-byte stores per tile column.
-  if (t.n0 + CFG::BN <= t.N && t.rows >= CFG::BM) {
+  // whose columns all lie inside the matrix take a path with no per-lane
+  // column test (rows past the edge, as in a MoE expert's last row tile, are
+  // skipped per lane): with the column test and its element-wise tail in the
+  // same code, the compiler merged the two into four predicated 4-byte
+  // stores per tile column.
+  if (t.n0 + CFG::BN <= t.N) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t row = wm_e * CFG::WTM + 16 * i + l16_e;
+      if (row >= t.rows) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int64_t col = t.n0 + wn_e * CFG::WTN + 16 * j + 4 * lq_e;
