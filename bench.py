@@ -42,8 +42,8 @@ QUANT_BYTES_BLOCK = 2 + 1 + 4 / (128 * 128)
 # same counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0,
 # WRITE_SIZE x1.0).  Valid only for the GEMM source it was measured on
 # (sha256 below); reported as null otherwise.
-GEMM_TRAFFIC = {"sha256": "09d36a767c39897b7835e4b8f6bfd12adf918adb96ce2d987fb5a8c776781e7b",
-                "fetch_bytes": 178242461, "write_bytes": 67108992}
+GEMM_TRAFFIC = {"sha256": "26ea86461f573339b4593c5ce99110ae7d4b34a5e9b305722c7cd01d3c78c282",
+                "fetch_bytes": 178245334, "write_bytes": 67108864}
 
 
 def parse():

@@ -346,13 +346,14 @@ struct CopyPlan {
 };
 
 // Whether a kernel issues the next group's copies from inside its row loop
-// (the power-of-two path of tiles with ILV_MIN_TM or more row tiles per
-// wave) instead of all at the group start.
+// (tiles with ILV_MIN_TM or more row tiles per wave) instead of all at the
+// group start.  Measured: +8 % on the power-of-two Fprop, +2-3 % on the fold
+// Fprop; on 128x128 tiles (two workgroups per CU) it cost 5 %.
 #ifndef FP8BLK_ILV_MIN_TM
 #define FP8BLK_ILV_MIN_TM 8
 #endif
 template <class CFG, bool P2>
-constexpr bool interleaved_copies() { return P2 && CFG::TM >= FP8BLK_ILV_MIN_TM; }
+constexpr bool interleaved_copies() { return CFG::TM >= FP8BLK_ILV_MIN_TM; }
 
 // One K group of MFMAs and scale folds on operands already in LDS (`ops`:
 // A tile then B tile; `sc`: row scales in lane order, then column/block
@@ -390,8 +391,8 @@ __device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s
 
 // LEAN_SC: form the row-scale addresses per group from an opaque copy of the
 // thread id (fewer live registers across the K loop, at a small cost in
-// issue); the kernels whose epilogue quantizes on store need it to stay
-// free of spills.
+// issue); the fold kernels with interleaved copies and the kernels whose
+// epilogue quantizes on store need it to stay free of spills.
 template <class CFG, bool OPB_T, bool ROW128, bool P2, bool LEAN_SC = false>
 __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
                                               v4f (&acc)[CFG::TM][CFG::TN],
@@ -412,7 +413,8 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
     // The two 16-byte halves are read in an order alternating with bit 4 of
     // the lane, so that the 32 lanes of each half-wave read 32 distinct
     // 16-byte slots (all four 16-lane groups need the same scales).  This
-    // form measured 2-3% slower in the kernels that do not need it.
+    // form measured 2-3% slower in the power-of-two kernels, which do not
+    // need it.
     int tid_s = tid;
     asm volatile("" : "+v"(tid_s));
     const int flip = (tid_s >> 4) & 1;
@@ -544,10 +546,26 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
     }
   };
   v4f ring[2];
+  // With interleaved copies the next group's copies are issued one or two
+  // per row tile here too (as in the power-of-two path, without fences).
+  using Plan = CopyPlan<CFG, OPB_T, ROW128>;
+  constexpr int LOADS = Plan::LOADS;
+  constexpr bool ILV = interleaved_copies<CFG, P2>();
+  typename Plan::Rsrc cr;
+  if constexpr (ILV) {
+    cr = plan.rsrc(t, gnext >= 0 ? gnext : t.g0);
+    const int on = gnext >= 0 ? -1 : 0;
+    cr.a[2] &= on; cr.b[2] &= on; cr.sa[2] &= on; cr.sb[2] &= on;
+  }
   v8i afr = load_a(0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
+    if constexpr (ILV) {
+#pragma unroll
+      for (int n = (i * LOADS) / TM; n < ((i + 1) * LOADS) / TM; ++n)
+        plan.template issue_one<true>(cr.a, cr.b, cr.sa, cr.sb, n, t, nbuf, nsbuf);
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int k = i * TN + j;
@@ -590,14 +608,14 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     __syncthreads();
     if (!ILV && g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q)>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
+    compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
     if (g + 1 < G) {
       wait_vmcnt<0>();
       __syncthreads();
       if (!ILV && g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q)>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
+      compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
