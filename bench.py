@@ -228,7 +228,13 @@ def main():
     def avg(k):
         return sum(hev.ms(a, b) for a, b in ev[k]) / len(ev[k])
 
+    def pct(k):
+        """10th, 50th and 90th percentile (us) of the launches recorded under k."""
+        ts = sorted(hev.ms(a, b) for a, b in ev[k])
+        return {f"p{q}_us": round(ts[min(len(ts) - 1, len(ts) * q // 100)] * 1e3, 2) for q in (10, 50, 90)}
+
     t_g = avg("gemm")
+    p_g = pct("gemm")
     # Second pass, outside the timed region: the same steps with events
     # between all three kernels, for the quantizers' durations.
     for i in range(args.steps):
@@ -239,10 +245,12 @@ def main():
     q1_gbs = M * K * QUANT_BYTES_1X128 / (t_q1 * 1e-3) / 1e9
     qb_gbs = K * N * QUANT_BYTES_BLOCK / (t_qb * 1e-3) / 1e9
     kernels = {
-        "quantize_1x128": {"us": round(t_q1 * 1e3, 2), "GB/s": round(q1_gbs, 1), "frac_hbm": round(q1_gbs / HBM_PEAK_GBS, 4)},
-        "quantize_block128": {"us": round(t_qb * 1e3, 2), "GB/s": round(qb_gbs, 1), "frac_hbm": round(qb_gbs / HBM_PEAK_GBS, 4)},
+        "quantize_1x128": {"us": round(t_q1 * 1e3, 2), "GB/s": round(q1_gbs, 1), "frac_hbm": round(q1_gbs / HBM_PEAK_GBS, 4),
+                           **pct("q1x128")},
+        "quantize_block128": {"us": round(t_qb * 1e3, 2), "GB/s": round(qb_gbs, 1), "frac_hbm": round(qb_gbs / HBM_PEAK_GBS, 4),
+                              **pct("qblock")},
         "gemm_fp8_blockscaled": {"us": round(t_g * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
-                                 "frac_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4)},
+                                 "frac_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), **p_g},
     }
 
     extras = {}
@@ -337,6 +345,17 @@ def run_extras(torch, fb, synthetic, dev, np):
     """Per-kernel timings on the other workloads (HIP events, few reps)."""
     res = {}
     reps = 10
+    # launch floor: the smallest launches of the library (one quantizer
+    # workgroup, one 128x128x128 GEMM tile), beside which the small workloads'
+    # times can be read
+    x1 = torch.ones(1, 128, dtype=torch.bfloat16, device=dev)
+    q1, s1 = fb.quantize_1x128(x1)
+    b1, sb1 = fb.quantize_block128(torch.ones(128, 128, dtype=torch.bfloat16, device=dev))
+    a1, sa1 = fb.quantize_1x128(torch.ones(128, 128, dtype=torch.bfloat16, device=dev))
+    c1 = torch.empty(128, 128, dtype=torch.float32, device=dev)
+    res["launch_floor"] = {
+        "quantize_1x128_1x128_us": round(timed_events(torch, lambda i: fb.quantize_1x128(x1, q=q1, s=s1), 40) * 1e3, 2),
+        "gemm_128x128x128_us": round(timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(a1, sa1, b1, sb1, C=c1), 40) * 1e3, 2)}
     # backward: Dgrad dX = dY W^T (OP_T), Wgrad dW = X^T dY (128x1 operands, ROW128)
     X, W, dY = synthetic.backward()
     Xd, Wd, dYd = X.to(dev), W.to(dev), dY.to(dev)
