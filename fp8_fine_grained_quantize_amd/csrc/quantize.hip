@@ -168,7 +168,20 @@ __global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restric
 // token_groups.h); workgroup row blockIdx.y is one group slot, a slot past
 // the last expert's groups exits, and the tokens of a partial group beyond
 // the expert's end are stored as code 0 so that the GEMM reads zeros there.
+//
+// The dense case uses k_quant_128x1_c64: 128 tokens x 64 channels per
+// workgroup, lane (rb = tid/8, cl = tid%8) holding tokens 4rb..4rb+3 of
+// channels 8cl..8cl+7; a lane's 4 codes of one channel are a 4-byte segment
+// of the LDS tile, and the segments move in groups of four (XOR by a
+// multiple of 4 taken from channel/8) so that the lanes of one LDS store hit
+// distinct banks while each 16-byte read of the store phase stays
+// contiguous.  Measured against 128 channels (rotating sets, one box): +3 %
+// on X [4096][7168], +14 % on dY [4096][2048]; the grouped case keeps 128
+// channels, where every workgroup scans the expert offsets and twice the
+// workgroups cost 7 % on dOut [65536][7168].
 // ---------------------------------------------------------------------------
+constexpr int Q128X1_CW = 64;
+
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   const uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
   const uint32_t hi = max(a >> 16, b >> 16);
@@ -288,6 +301,110 @@ __global__ __launch_bounds__(256) void k_quant_128x1(const uint16_t* __restrict_
       *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     } else {
       const uint32_t wds[4] = {lo.x, lo.y, hi.x, hi.y};
+      for (int j = 0; j < 16 && o + j < o_end; ++j) dst[j] = (uint8_t)((wds[j >> 2] >> ((j & 3) * 8)) & 0xFF);
+    }
+  }
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quant_128x1_c64(const uint16_t* __restrict__ x, int64_t T, int64_t C,
+                                                          int64_t ldx, uint8_t* __restrict__ qT, int64_t ldqT,
+                                                          float* __restrict__ s) {
+  constexpr int CW = Q128X1_CW, LPR = CW / 8, RB = 256 / LPR, TPL = 128 / RB;
+  static_assert(TPL == 4, "4-byte token segments");
+  __shared__ uint32_t red[4][LPR][4];
+  __shared__ float sh_s[CW], sh_r[CW];
+  __shared__ int sh_slow[CW];
+  __shared__ __align__(16) uint8_t tile[CW * 128];
+  const int64_t c0 = (int64_t)blockIdx.x * CW;
+  const int64_t t0 = (int64_t)blockIdx.y * 128, t_end = T;
+  const int64_t o0 = t0, o_end = T;
+  const int tid = threadIdx.x;
+  const int cl = tid % LPR;
+  const int rb = tid / LPR;
+  const int64_t col = c0 + cl * 8;
+  const int64_t avail = C - col;
+  uint4 v[TPL];
+  uint32_t m2[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < TPL; ++j) {
+    const int64_t t = t0 + rb * TPL + j;
+    v[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (t < t_end && avail > 0) v[j] = load_chunk8(x + t * ldx + col, avail);
+  }
+#pragma unroll
+  for (int j = 0; j < TPL; ++j) {
+    m2[0] = pk_max_u16(m2[0], v[j].x & 0x7FFF7FFFu);
+    m2[1] = pk_max_u16(m2[1], v[j].y & 0x7FFF7FFFu);
+    m2[2] = pk_max_u16(m2[2], v[j].z & 0x7FFF7FFFu);
+    m2[3] = pk_max_u16(m2[3], v[j].w & 0x7FFF7FFFu);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int d = LPR; d < 64; d <<= 1) m2[i] = pk_max_u16(m2[i], (uint32_t)__shfl_xor((int)m2[i], d));
+  }
+  if ((tid & 63) < LPR) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[tid >> 6][cl][i] = m2[i];
+  }
+  __syncthreads();
+  if (tid < CW) {
+    const int c = tid, cc = c >> 3, pair = (c & 7) >> 1, half = c & 1;
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t d = red[w][cc][pair];
+      a = max(a, half ? (d >> 16) : (d & 0xFFFFu));
+    }
+    const TileScale ts = make_scale<POW2, true>(a << 16);
+    sh_s[c] = ts.s;
+    sh_r[c] = ts.r;
+    sh_slow[c] = ts.slow ? 1 : 0;
+    if (c0 + c < C) s[(int64_t)blockIdx.y * C + c0 + c] = ts.s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = cl * 8 + i;
+    TileScale ts;
+    ts.s = sh_s[c];
+    ts.r = sh_r[c];
+    ts.slow = sh_slow[c] != 0;
+    float y[TPL];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) {
+      const uint32_t wd = (i >> 1) == 0 ? v[j].x : (i >> 1) == 1 ? v[j].y : (i >> 1) == 2 ? v[j].z : v[j].w;
+      y[j] = quotient_fast<POW2, true>((i & 1) ? bf16_hi(wd) : bf16_lo(wd), ts);
+    }
+    if (__builtin_expect(ts.slow, 0)) {
+#pragma unroll
+      for (int j = 0; j < TPL; ++j) {
+        const uint32_t wd = (i >> 1) == 0 ? v[j].x : (i >> 1) == 1 ? v[j].y : (i >> 1) == 2 ? v[j].z : v[j].w;
+        y[j] = quotient_slow((i & 1) ? bf16_hi(wd) : bf16_lo(wd), ts.s);
+      }
+    }
+    const uint32_t codes = pack4_e4m3(y[0], y[1], y[2], y[3]);
+    // 4-byte token segment rb of channel c; segments move in groups of four
+    // (XOR by a multiple of 4) so a 16-byte read of the store phase stays
+    // contiguous, and lanes of different cl land on different banks
+    const int seg = rb ^ (4 * (cl & 7));
+    *reinterpret_cast<uint32_t*>(tile + c * 128 + seg * 4) = codes;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < CW / 32; ++k) {
+    const int chunk = tid + 256 * k;
+    const int c = chunk >> 3;
+    const int part = chunk & 7;  // tokens 16*part .. 16*part+15
+    if (c0 + c >= C) continue;
+    const uint4 w = *reinterpret_cast<const uint4*>(tile + c * 128 + (((4 * part) ^ (4 * ((c >> 3) & 7))) * 4));
+    const int64_t o = o0 + 16 * part;
+    uint8_t* dst = qT + (c0 + c) * ldqT + o;
+    if (o + 16 <= o_end) {
+      *reinterpret_cast<uint4*>(dst) = w;
+    } else {
+      const uint32_t wds[4] = {w.x, w.y, w.z, w.w};
       for (int j = 0; j < 16 && o + j < o_end; ++j) dst[j] = (uint8_t)((wds[j >> 2] >> ((j & 3) * 8)) & 0xFF);
     }
   }
@@ -465,17 +582,15 @@ extern "C" fp8blk_status_t fp8blk_quantize_128x1(const uint16_t* x, int64_t T, i
                                                  int64_t ldqT, float* s, uint32_t flags, void* stream) {
   if (flags & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
   if (!matrix_ok(x, T, C, ldx, 2) || !matrix_ok(qT, C, T, ldqT, 1)) return FP8BLK_ERR_INVALID_ARG;
-  const int64_t GT = ceil_div(T, 128), GC = ceil_div(C, 128);
+  const int64_t GT = ceil_div(T, 128), GC = ceil_div(C, Q128X1_CW);
   if (!vec_ok(s, GT * C)) return FP8BLK_ERR_INVALID_ARG;
   if (T == 0 || C == 0) return FP8BLK_OK;
   if (GC > 0x7FFFFFFF || GT > 65535) return FP8BLK_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)GC, (unsigned)GT);
   if (flags & FP8BLK_SCALE_POW2)
-    hipLaunchKernelGGL((k_quant_128x1<true, false>), grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT,
-                       s, nullptr, (int64_t)0);
+    hipLaunchKernelGGL(k_quant_128x1_c64<true>, grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT, s);
   else
-    hipLaunchKernelGGL((k_quant_128x1<false, false>), grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT,
-                       s, nullptr, (int64_t)0);
+    hipLaunchKernelGGL(k_quant_128x1_c64<false>, grid, dim3(256), 0, as_stream(stream), x, T, C, ldx, qT, ldqT, s);
   return launch_status();
 }
 
