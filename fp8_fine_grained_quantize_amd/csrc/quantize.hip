@@ -563,8 +563,10 @@ extern "C" fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R
   const int64_t GR = ceil_div(R, 128), GC = ceil_div(C, 128);
   if (!vec_ok(s, GR * GC)) return FP8BLK_ERR_INVALID_ARG;
   if (R == 0 || C == 0) return FP8BLK_OK;
-  // Persistent grid: 8 workgroups of 256 lanes per compute unit, each taking
-  // every grid-th block.
+  // Persistent grid of up to 8 workgroups of 256 lanes per compute unit, each
+  // taking every grid-th block.  At the kernel's register count 4 of them are
+  // resident per compute unit at a time and the rest start as those finish;
+  // smaller grids that keep every workgroup resident measured slower.
   constexpr int NT = 256;
   int64_t grid = GR * GC;
   const int64_t cap = (int64_t)device_cus() * 8;
