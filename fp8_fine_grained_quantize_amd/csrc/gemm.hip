@@ -599,6 +599,12 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (g0 < G) plan.issue(t, g0, ops0, sc0);  // no groups (an expert without tokens): C = 0
+  // A wave whose rows all lie past the tile's valid rows (the partial last
+  // row tile of an expert or of the matrix) skips its MFMAs and fold; it
+  // still issues its copies and meets every barrier.  With interleaved
+  // copies the copies sit inside compute_group, so every wave computes.
+  const int wrow0 = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / CFG::WAVES_N) * CFG::WTM;
+  const bool computes = ILV || wrow0 < t.rows;
   for (int g = g0; g < G; g += 2) {
     // Group g has landed in stage 0 once this lane's copies are complete;
     // after the barrier every wave's copies are visible and every wave is
@@ -608,14 +614,16 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     __syncthreads();
     if (!ILV && g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
+    if (computes)
+      compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
     __builtin_amdgcn_sched_barrier(0);
     if (g + 1 < G) {
       wait_vmcnt<0>();
       __syncthreads();
       if (!ILV && g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
+      if (computes)
+        compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
