@@ -37,6 +37,9 @@ What the pages fix, and the readings taken where they are silent:
     partial into a full-precision accumulator, multiplying in the group's
     scales [p2¶3, p2¶4].  Here the partial is exact (FP64, see
     ``gemm_blockscaled``) and the accumulator is FP64.
+  * Context only, with no HIP counterpart: the limited-accumulation
+    emulation at the end of this file.  Its rule is pinned against brute
+    force; whether the rule matches the H800 is parity unpinned.
 """
 from __future__ import annotations
 
