@@ -80,6 +80,29 @@ def test_block128_past_2g_elements():
     _free()
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_block128_one_wave_per_block(pow2):
+    """Above 6144 blocks quantize_block128 takes one wave per block; ragged
+    row and column edges, outlier columns, both scale modes."""
+    R, C = 10000, 10016
+    assert (-(-R // 128)) * (-(-C // 128)) > 6144
+    print(f"[max] quantize_block128 one wave per block [{R}][{C}] pow2={pow2}", flush=True)
+    g = torch.Generator().manual_seed(31)
+    x = synthetic.randn_bf16((R, C), 1.0, g, outlier_cols=3, outlier_factor=60.0).cuda()
+    q, s = fb.quantize_block128(x, pow2=pow2)
+    torch.cuda.synchronize()
+    GR, GC = -(-R // 128), -(-C // 128)
+    rng = np.random.default_rng(3)
+    picks = [(0, 0), (0, GC - 1), (GR - 1, 0), (GR - 1, GC - 1)] + [tuple(v) for v in rng.integers(0, [GR, GC], (8, 2))]
+    for bi, bj in picks:
+        rs, cs = slice(128 * bi, min(R, 128 * bi + 128)), slice(128 * bj, min(C, 128 * bj + 128))
+        qo, so = oracle.quantize_block128(bf16_bits(x[rs, cs].cpu()), pow2=pow2)
+        assert np.array_equal(np_u8(q[rs, cs]), qo), (bi, bj)
+        assert np_f32(s[bi, bj]).view(np.uint32) == so[0, 0].view(np.uint32), (bi, bj)
+    del x, q, s
+    _free()
+
+
 @pytest.mark.parametrize("out", ["fp32", "bf16"])
 def test_gemm_output_past_2g_elements(out):
     M, N, K = 65666, 32848, 256
