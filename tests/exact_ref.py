@@ -129,3 +129,33 @@ def quantize_values(xs, pow2: bool):
         y = round_to_f32(v / Fraction(s), negative_zero=neg)
         codes.append(e4m3_nearest(y))
     return codes, s
+
+
+# ---- limited-precision accumulation, exactly -------------------------------
+
+
+def _expo(t: Fraction) -> int:
+    """E with 2^(E-1) <= |t| < 2^E, t != 0."""
+    t = abs(t)
+    e = t.numerator.bit_length() - t.denominator.bit_length()
+    fl = e if t >= Fraction(2) ** e else e - 1
+    return fl + 1
+
+
+def limited_dot_exact(a, b, width: int, bits: int) -> float:
+    """The limited-accumulation reading (each step aligns `width` products
+    and the running sum to the largest term, truncates every term toward zero
+    to a multiple of 2^(E - bits), and rounds the exact sum of the kept terms
+    to binary32) evaluated with Python fractions and integer truncation.
+    a, b: sequences of exact FP8 values (floats)."""
+    acc = Fraction(0)
+    for k0 in range(0, len(a), width):
+        terms = [acc] + [Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a[k0:k0 + width], b[k0:k0 + width])]
+        nz = [t for t in terms if t != 0]
+        if not nz:
+            acc = Fraction(0)
+            continue
+        lsb = Fraction(2) ** (max(_expo(t) for t in nz) - bits)
+        s = sum(int(t / lsb) * lsb for t in terms)  # int() truncates toward zero
+        acc = Fraction(round_to_f32(s))
+    return float(acc)

@@ -24,6 +24,7 @@ import torch
 import oracle
 import synthetic
 from synthetic import bf16_bits
+from tests import exact_ref
 
 
 def _fp8_values(rng, shape, zero_frac=0.1):
@@ -33,26 +34,8 @@ def _fp8_values(rng, shape, zero_frac=0.1):
     return oracle.e4m3_decode(codes)
 
 
-def _expo(t: Fraction) -> int:
-    """E with 2^(E-1) <= |t| < 2^E, t != 0."""
-    t = abs(t)
-    e = t.numerator.bit_length() - t.denominator.bit_length()
-    fl = e if t >= Fraction(2) ** e else e - 1
-    return fl + 1
-
-
 def _brute(a, b, width, bits):
-    acc = Fraction(0)
-    for k0 in range(0, len(a), width):
-        terms = [acc] + [Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a[k0:k0 + width], b[k0:k0 + width])]
-        nz = [t for t in terms if t != 0]
-        if not nz:
-            acc = Fraction(0)
-            continue
-        lsb = Fraction(2) ** (max(_expo(t) for t in nz) - bits)
-        s = sum(int(t / lsb) * lsb for t in terms)  # int() truncates toward zero
-        acc = Fraction(float(np.float32(float(s))))  # float(s) is exact (< 53 bits)
-    return float(acc)
+    return exact_ref.limited_dot_exact(a, b, width, bits)
 
 
 @pytest.mark.parametrize("width,bits", [(1, 3), (4, 5), (8, 14), (32, 14), (7, 20)])
