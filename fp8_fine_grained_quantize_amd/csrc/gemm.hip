@@ -259,16 +259,10 @@ struct CopyPlan {
     }
   }
 
-  // Per-lane byte offset of this lane's scale copy, recomputed at each issue
-  // from an opaque copy of the thread id: a few integer operations per group,
-  // one VGPR less held across the K loop (the 256x256 fold kernels run at
-  // the register limit).  SEL: both offsets are formed and one is selected.
-  // Copies issued from inside a row loop need that: there a branch would
-  // split the loop into two blocks, and the compiler then sinks every MFMA
-  // of the group below it, past the scheduling fences.  The copies issued at
-  // the group start keep the branch, which leaves the BF16-output fold
-  // kernel one register short of a spill.
-  template <bool SEL>
+  // Per-lane byte offset of this lane's scale copy.  The 128x128 kernels
+  // form it at each issue from an opaque copy of the thread id (a few
+  // integer operations per group instead of a VGPR held across the K loop);
+  // the row-pipelined loop forms it once per tile.
   __device__ __forceinline__ uint32_t sc_offset(const TileArgs& t) const {
     constexpr int TM = CFG::TM, WTM = CFG::WTM;
     int tid = threadIdx.x;
@@ -285,7 +279,6 @@ struct CopyPlan {
     // n0/128 + (p - BM) (only the first BN/128 positions are used)
     const uint32_t col_off =
         ROW128 ? (uint32_t)((p - BM) * 4) : (uint32_t)((p - BM) * (OPB_T ? (int)(t.K >> 7) : 1) * 4);
-    if constexpr (SEL) return blk * 64 < BM ? row_off : col_off;
     if (blk * 64 < BM) return row_off;
     return col_off;
   }
@@ -324,7 +317,6 @@ struct CopyPlan {
   // Copy number n (0 .. LOADS-1) of a group: A blocks, then B blocks, then
   // the scale block.
   static constexpr int LOADS = CFG::A_ITERS + CFG::B_ITERS + 1;
-  template <bool SEL = false>
   __device__ __forceinline__ void issue_one(v4i ra, v4i rb,
                                             v4i rsa, v4i rsb, int n,
                                             const TileArgs& t, uint8_t* buf, float* sbuf) const {
@@ -340,20 +332,20 @@ struct CopyPlan {
       const int blk = wave < CFG::S_BLOCKS ? wave : 0;
       const bool rows = blk * 64 < BM;  // wave-uniform; a select keeps the copy branch-free
       const v4i rs = v4i{rows ? rsa[0] : rsb[0], rows ? rsa[1] : rsb[1], rows ? rsa[2] : rsb[2], rows ? rsa[3] : rsb[3]};
-      dma4(rs, sc_offset<SEL>(t), (uint8_t*)(sbuf + blk * 64));
+      dma4(rs, sc_offset(t), (uint8_t*)(sbuf + blk * 64));
     }
   }
 };
 
-// Whether a kernel issues the next group's copies from inside its row loop
-// (tiles with ILV_MIN_TM or more row tiles per wave) instead of all at the
-// group start.  Measured: +8 % on the power-of-two Fprop, +2-3 % on the fold
-// Fprop; on 128x128 tiles (two workgroups per CU) it cost 5 %.
-#ifndef FP8BLK_ILV_MIN_TM
-#define FP8BLK_ILV_MIN_TM 8
+// Whether a tile runs the row-pipelined K loop (gemm_loop_rows below): tiles
+// with ROWPIPE_MIN_TM or more row tiles per wave (the 256x256 tile).  The
+// 128x128 tiles (two workgroups per CU) keep the loop that issues a group's
+// copies at its start (compute_group below).
+#ifndef FP8BLK_ROWPIPE_MIN_TM
+#define FP8BLK_ROWPIPE_MIN_TM 8
 #endif
-template <class CFG, bool P2>
-constexpr bool interleaved_copies() { return CFG::TM >= FP8BLK_ILV_MIN_TM; }
+template <class CFG, bool ROW128>
+constexpr bool row_pipelined() { return CFG::TM >= FP8BLK_ROWPIPE_MIN_TM && !ROW128; }
 
 // One K group of MFMAs and scale folds on operands already in LDS (`ops`:
 // A tile then B tile; `sc`: row scales in lane order, then column/block
@@ -389,15 +381,11 @@ __device__ __forceinline__ v4f mfma_e8m0_sel(int oa, int ob, const v8i& a, const
 // E8M0 code of a power-of-two FP32 scale: its biased exponent.
 __device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
 
-// LEAN_SC: form the row-scale addresses per group from an opaque copy of the
-// thread id (fewer live registers across the K loop, at a small cost in
-// issue); the fold kernels with interleaved copies and the kernels whose
-// epilogue quantizes on store need it to stay free of spills.
-template <class CFG, bool OPB_T, bool ROW128, bool P2, bool LEAN_SC = false>
+// One K group on the 128x128 tiles: the group's copies were issued at its
+// start by the caller.
+template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
-                                              v4f (&acc)[CFG::TM][CFG::TN],
-                                              const CopyPlan<CFG, OPB_T, ROW128>& plan, const TileArgs& t, int gnext,
-                                              uint8_t* nbuf, float* nsbuf) {
+                                              v4f (&acc)[CFG::TM][CFG::TN]) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -409,30 +397,10 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
 
   // Row scales of this lane's TM row tiles (contiguous by the copy plan).
   float sa[TM];
-  if constexpr (LEAN_SC && TM % 8 == 0) {
-    // The two 16-byte halves are read in an order alternating with bit 4 of
-    // the lane, so that the 32 lanes of each half-wave read 32 distinct
-    // 16-byte slots (all four 16-lane groups need the same scales).  This
-    // form measured 2-3% slower in the power-of-two kernels, which do not
-    // need it.
-    int tid_s = tid;
-    asm volatile("" : "+v"(tid_s));
-    const int flip = (tid_s >> 4) & 1;
-    const float* srow = sc + wm * CFG::WTM + (tid_s & 15) * TM;
 #pragma unroll
-    for (int i = 0; i < TM; i += 8) {
-      const float4 v0 = *reinterpret_cast<const float4*>(srow + i + 4 * flip);
-      const float4 v1 = *reinterpret_cast<const float4*>(srow + i + 4 * (flip ^ 1));
-      const float4 lo = flip ? v1 : v0, hi = flip ? v0 : v1;
-      sa[i] = lo.x; sa[i + 1] = lo.y; sa[i + 2] = lo.z; sa[i + 3] = lo.w;
-      sa[i + 4] = hi.x; sa[i + 5] = hi.y; sa[i + 6] = hi.z; sa[i + 7] = hi.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
-      sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
-    }
+  for (int i = 0; i < TM; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
+    sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
   }
   // Column scales: one block value per wave, or four per column tile.
   float4 sbv[TN];
@@ -494,32 +462,12 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
     } else {
       sbe = e8m0_of(sbb);
     }
-    // The copies of group gnext are spread over the row tiles (issued all at
-    // the group start they hold up the first MFMAs); with no next group
-    // (gnext < 0) the resources get a zero record count, so the same
-    // instructions read nothing and the loop has no branch.  A fragments are
-    // read two row tiles ahead, and a scheduling fence after each row tile
-    // keeps the next reads and copies from being hoisted above its MFMAs.
-    using Plan = CopyPlan<CFG, OPB_T, ROW128>;
-    constexpr int LOADS = Plan::LOADS;
-    constexpr bool ILV = interleaved_copies<CFG, P2>();
-    typename Plan::Rsrc cr;
-    if constexpr (ILV) {
-      cr = plan.rsrc(t, gnext >= 0 ? gnext : t.g0);
-      const int on = gnext >= 0 ? -1 : 0;
-      cr.a[2] &= on; cr.b[2] &= on; cr.sa[2] &= on; cr.sb[2] &= on;
-    }
     v8i af[TM];
     af[0] = load_a(0);
     if (TM > 1) af[1] = load_a(1);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i + 2 < TM) af[i + 2] = load_a(i + 2);
-      if constexpr (ILV) {
-#pragma unroll
-        for (int n = (i * LOADS) / TM; n < ((i + 1) * LOADS) / TM; ++n)
-          plan.template issue_one<true>(cr.a, cr.b, cr.sa, cr.sb, n, t, nbuf, nsbuf);
-      }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = mfma_e8m0_sel(ROW128 ? j : 0, i % 4, bfr[j], af[i], acc[i][j], sbe, sae[i / 4]);
@@ -546,26 +494,10 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
     }
   };
   v4f ring[2];
-  // With interleaved copies the next group's copies are issued one or two
-  // per row tile here too (as in the power-of-two path, without fences).
-  using Plan = CopyPlan<CFG, OPB_T, ROW128>;
-  constexpr int LOADS = Plan::LOADS;
-  constexpr bool ILV = interleaved_copies<CFG, P2>();
-  typename Plan::Rsrc cr;
-  if constexpr (ILV) {
-    cr = plan.rsrc(t, gnext >= 0 ? gnext : t.g0);
-    const int on = gnext >= 0 ? -1 : 0;
-    cr.a[2] &= on; cr.b[2] &= on; cr.sa[2] &= on; cr.sb[2] &= on;
-  }
   v8i afr = load_a(0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
-    if constexpr (ILV) {
-#pragma unroll
-      for (int n = (i * LOADS) / TM; n < ((i + 1) * LOADS) / TM; ++n)
-        plan.template issue_one<true>(cr.a, cr.b, cr.sa, cr.sb, n, t, nbuf, nsbuf);
-    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int k = i * TN + j;
@@ -579,6 +511,249 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
   fold(ring[(TM * TN - 1) & 1], TM - 1, TN - 1);
 }
 
+// ---- Row-pipelined K loop (256x256 tiles) ---------------------------------
+// After each group's barrier a wave reads its B fragments and first A
+// fragment, then walks its TM row tiles: row tile i reads the A fragment of
+// row i+1, issues (in the first FP8BLK_COPY_ROWS rows) its share of the next
+// group's copies, and runs its TN MFMAs; the fold path folds each partial
+// FP8BLK_FOLD_RING-1 MFMAs after it was issued.  The copy resources advance
+// from per-tile cursors held in scalar registers and the scale copy's lane
+// offset is computed once per tile, so a group issues little beyond its
+// MFMAs, folds, LDS reads and copies.
+// Measured on the 4096x4096x7168 Fprop (interleaved on one box, results
+// bitwise identical): cursors and once-per-tile offsets against per-group
+// recomputation -9 %; copies spread over the first 4 of 8 rows against all
+// rows -5 %, against the first 1 / 2 / 3 rows -4 / -3 / -5 %; fold ring 4
+// against 2 and 3 -3 %.  Ablations (timing only): without the copies -17 %,
+// without the A and B fragment reads -18 %, without the barrier -11 %,
+// without any MFMA -12 %: the loop is bound by moving the operands (a
+// copy-only loop of the same traffic takes half the GEMM's time, and copies
+// overlap the MFMAs only in part), not by the matrix cores.
+#ifndef FP8BLK_FOLD_RING
+#define FP8BLK_FOLD_RING 4
+#endif
+#ifndef FP8BLK_COPY_ROWS
+#define FP8BLK_COPY_ROWS 4
+#endif
+
+// Copy resources of the next K group: A tile, B tile and this wave's scale
+// run, each a 64-bit address advanced by a fixed stride per group.
+template <class CFG, bool OPB_T>
+struct GroupCursor {
+  uint64_t a, b, s;
+  int64_t b_step, s_step;
+  int64_t b_left;  // valid bytes from b on ([K][N] B: shrinks per group)
+  int32_t a_cnt, s_cnt;
+
+  __device__ __forceinline__ void init(const TileArgs& t, int g, bool rows_wave) {
+    constexpr int BN = CFG::BN;
+    const int64_t Gk = t.K / 128, NB = (t.N + 127) / 128, nb0 = t.n0 / 128;
+    a = reinterpret_cast<uint64_t>(t.A) + (uint64_t)g * 128;
+    a_cnt = (int32_t)((t.rows - 1) * t.lda + 128);
+    if (OPB_T) {
+      b = reinterpret_cast<uint64_t>(t.B + t.n0 * t.ldb) + (uint64_t)g * 128;
+      const int64_t nvalid = t.N - t.n0 < BN ? t.N - t.n0 : BN;
+      b_left = (nvalid - 1) * t.ldb + 128;
+      b_step = 128;
+    } else {
+      b = reinterpret_cast<uint64_t>(t.B + t.n0) + (uint64_t)g * 128 * t.ldb;
+      b_left = (t.K - (int64_t)g * 128) * t.ldb - t.n0;
+      b_step = 128 * t.ldb;
+    }
+    if (rows_wave) {
+      s = reinterpret_cast<uint64_t>(t.sA + (int64_t)g * t.sA_ld);
+      s_step = t.sA_ld * 4;
+      s_cnt = (int32_t)(t.rows * 4);
+    } else if (OPB_T) {
+      s = reinterpret_cast<uint64_t>(t.sB + nb0 * Gk + g);
+      s_step = 4;
+      s_cnt = (int32_t)(((NB - nb0 - 1) * Gk + 1) * 4);
+    } else {
+      s = reinterpret_cast<uint64_t>(t.sB + (int64_t)g * t.sB_ld + nb0);
+      s_step = t.sB_ld * 4;
+      s_cnt = (int32_t)((NB - nb0) * 4);
+    }
+  }
+  __device__ __forceinline__ void advance() {
+    a += 128;
+    b += b_step;
+    if (!OPB_T) b_left -= b_step;
+    s += s_step;
+  }
+  // Resources; `on` false gives a zero record count (every copy reads nothing).
+  static __device__ __forceinline__ v4i rsrc(uint64_t addr, int64_t n) {
+    const int32_t c = n > 0x7FFFFFFF ? 0x7FFFFFFF : (n < 0 ? 0 : (int32_t)n);
+    return v4i{(int)(uint32_t)addr, (int)((uint32_t)(addr >> 32) & 0xFFFFu), c, 0x00020000};
+  }
+  __device__ __forceinline__ v4i ra(bool on) const { return rsrc(a, on ? a_cnt : 0); }
+  __device__ __forceinline__ v4i rb(bool on) const { return rsrc(b, on ? b_left : 0); }
+  __device__ __forceinline__ v4i rs(bool on) const { return rsrc(s, on ? s_cnt : 0); }
+};
+
+// Copies n0 .. n1-1 of a group (A blocks, then B blocks, then the scale run).
+template <class CFG, bool OPB_T>
+__device__ __forceinline__ void issue_copies(const TileArgs& t, const CopyPlan<CFG, OPB_T, false>& plan,
+                                             uint32_t scoff, const v4i& ra, const v4i& rb, const v4i& rs, int n0,
+                                             int n1, uint8_t* buf, float* sbuf, int wave, int blk) {
+  constexpr int NW = CFG::NW, KSTEP = CopyPlan<CFG, OPB_T, false>::KSTEP;
+#pragma unroll
+  for (int n = n0; n < n1; ++n) {
+    if (n < CFG::A_ITERS) {
+      dma16(ra, plan.a, (int32_t)(n * 8 * NW * t.lda), buf + (n * NW + wave) * 1024);
+    } else if (n < CFG::A_ITERS + CFG::B_ITERS) {
+      const int it = n - CFG::A_ITERS;
+      const int32_t so = OPB_T ? (int32_t)(it * 8 * NW * t.ldb) : (int32_t)(it * KSTEP * t.ldb);
+      dma16(rb, (!OPB_T && (it & 1)) ? plan.b2 : plan.b, so, buf + CFG::A_BYTES + (it * NW + wave) * 1024);
+    } else {
+      dma4(rs, scoff, (uint8_t*)(sbuf + blk * 64));
+    }
+  }
+}
+
+// One K group of a row-pipelined tile: operands of this group in `ops`/`sc`,
+// the next group's copies (resources ra/rb/rs) into `nops`/`nsc`.
+template <class CFG, bool OPB_T, bool P2>
+__device__ __forceinline__ void compute_group_rows(const uint8_t* ops, const float* sc, v4f (&acc)[CFG::TM][CFG::TN],
+                                                   const TileArgs& t, const CopyPlan<CFG, OPB_T, false>& plan,
+                                                   uint32_t scoff, const v4i& ra, const v4i& rb, const v4i& rs,
+                                                   uint8_t* nops, float* nsc, int wave, int blk) {
+  constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN, R = FP8BLK_FOLD_RING;
+  constexpr int LOADS = CopyPlan<CFG, OPB_T, false>::LOADS, CR = FP8BLK_COPY_ROWS;
+  static_assert(CR >= 1 && CR <= TM, "copy rows");
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const uint8_t* As = ops;
+  const uint8_t* Bs = ops + CFG::A_BYTES;
+  auto load_a = [&](int i) {
+    const int r = wm * CFG::WTM + 16 * i + l16;
+    const uint4 lo = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq));
+    const uint4 hi = *reinterpret_cast<const uint4*>(As + kmaj_off(r, 2 * lq + 1));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  v8i afr = load_a(0);
+  v8i bfr[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int ncol = wn * CFG::WTN + 16 * j;
+    if (OPB_T) {
+      const int r = ncol + l16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + kmaj_off(r, 2 * lq));
+      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + kmaj_off(r, 2 * lq + 1));
+      bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else {
+      const int jj = l16 >> 1, h = l16 & 1;
+      v2i part[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = 32 * lq + 8 * r + jj;
+        part[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(Bs + nmaj_off<BN>(k, ncol >> 4) + 8 * h));
+      }
+      bfr[j] = v8i{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+    }
+  }
+  // Row scales of this lane's row tiles and the wave's block scale.
+  float sa[TM];
+#pragma unroll
+  for (int i = 0; i < TM; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
+    sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
+  }
+  const float sbb = sc[BM + (wn * CFG::WTN) / 128];
+
+  if constexpr (P2) {
+    // E8M0 exponents: row tile i in byte i%4 of sae[i/4]; the block scale.
+    uint32_t sae[(TM + 3) / 4];
+#pragma unroll
+    for (int q = 0; q < (TM + 3) / 4; ++q) sae[q] = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sae[i / 4] |= e8m0_of(sa[i]) << (8 * (i % 4));
+    const uint32_t sbe = e8m0_of(sbb);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
+      if (i < CR)
+        issue_copies<CFG, OPB_T>(t, plan, scoff, ra, rb, rs, (i * LOADS) / CR, ((i + 1) * LOADS) / CR, nops, nsc,
+                                 wave, blk);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_e8m0_sel(0, i % 4, bfr[j], afr, acc[i][j], sbe, sae[i / 4]);
+      afr = anext;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
+
+  float scl[TM];  // fl32(sA * sB) per row tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i) scl[i] = sa[i] * sbb;
+  v4f ring[R];
+  auto fold = [&](int kk) {
+    const int i = kk / TN, j = kk % TN;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(ring[kk % R][r], scl[i], acc[i][j][r]);
+  };
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
+    if (i < CR)
+      issue_copies<CFG, OPB_T>(t, plan, scoff, ra, rb, rs, (i * LOADS) / CR, ((i + 1) * LOADS) / CR, nops, nsc, wave,
+                               blk);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int k = i * TN + j;
+      // C^T tile: the B fragment is the row operand.
+      ring[k % R] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[j], afr, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0,
+                                                                     0, 127, 0, 127);
+      if (k >= R - 1) fold(k - (R - 1));
+    }
+    afr = anext;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int kk = TM * TN - (R - 1); kk < TM * TN; ++kk) fold(kk);
+}
+
+// The K loop of a row-pipelined tile (groups t.g0 .. t.g1-1).  Two groups per
+// iteration, one per LDS stage, with no branch inside the iteration (a
+// branch there lets the compiler sink the MFMAs of the first group below it,
+// past the row fences); an odd last group runs after the loop.
+template <class CFG, bool OPB_T, bool P2>
+__device__ __forceinline__ void gemm_loop_rows(const TileArgs& t, uint8_t* ops0, uint8_t* ops1, float* sc0, float* sc1,
+                                               v4f (&acc)[CFG::TM][CFG::TN]) {
+  const int g0 = t.g0, G = t.g1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int blk = wave < CFG::S_BLOCKS ? wave : 0;  // this wave's 64-float block of the scale buffer
+  CopyPlan<CFG, OPB_T, false> plan;
+  plan.init(t);
+  const uint32_t scoff = plan.sc_offset(t);
+  GroupCursor<CFG, OPB_T> cur;
+  cur.init(t, g0, blk * 64 < CFG::BM);
+  if (g0 < G)  // no groups (an expert without tokens): C = 0
+    issue_copies<CFG, OPB_T>(t, plan, scoff, cur.ra(true), cur.rb(true), cur.rs(true), 0,
+                             CopyPlan<CFG, OPB_T, false>::LOADS, ops0, sc0, wave, blk);
+  cur.advance();
+  auto step = [&](int gnext, uint8_t* ops, float* sc, uint8_t* nops, float* nsc) {
+    // This group has landed in `ops` once this lane's copies are complete;
+    // after the barrier every wave's copies are visible and every wave is
+    // done reading the other stage, which then receives group gnext.
+    wait_vmcnt<0>();
+    __syncthreads();
+    const bool on = gnext < G;
+    const v4i ra = cur.ra(on), rb = cur.rb(on), rs = cur.rs(on);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_group_rows<CFG, OPB_T, P2>(ops, sc, acc, t, plan, scoff, ra, rb, rs, nops, nsc, wave, blk);
+    __builtin_amdgcn_sched_barrier(0);
+    cur.advance();
+  };
+  int g = g0;
+  for (; g + 1 < G; g += 2) {
+    step(g + 1, ops0, sc0, ops1, sc1);
+    step(g + 2, ops1, sc1, ops0, sc0);
+  }
+  if (g < G) step(g + 1, ops0, sc0, ops1, sc1);
+  wait_vmcnt<0>();  // the last group's (empty) copies
+}
+
 // The whole K loop of one output tile.  ops0/ops1 and sc0/sc1 are distinct
 // LDS arrays (the two pipeline stages); the loop is unrolled by two so that
 // every access names its array at compile time, which lets the compiler see
@@ -588,47 +763,43 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
   constexpr int TM = CFG::TM, TN = CFG::TN;
   const int g0 = t.g0, G = t.g1;
 
-  constexpr bool ILV = interleaved_copies<CFG, P2>();
-  CopyPlan<CFG, OPB_T, ROW128> plan;
-  plan.init(t);
-
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (g0 < G) plan.issue(t, g0, ops0, sc0);  // no groups (an expert without tokens): C = 0
-  // A wave whose rows all lie past the tile's valid rows (the partial last
-  // row tile of an expert or of the matrix) skips its MFMAs and fold; it
-  // still issues its copies and meets every barrier.  With interleaved
-  // copies the copies sit inside compute_group, so every wave computes.
-  const int wrow0 = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / CFG::WAVES_N) * CFG::WTM;
-  const bool computes = ILV || wrow0 < t.rows;
-  for (int g = g0; g < G; g += 2) {
-    // Group g has landed in stage 0 once this lane's copies are complete;
-    // after the barrier every wave's copies are visible and every wave is
-    // done reading stage 1 (group g-1), which then receives group g+1 (with
-    // interleaved copies, from inside compute_group).
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (!ILV && g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (computes)
-      compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops0, sc0, acc, plan, t, ILV && g + 1 < G ? g + 1 : -1, ops1, sc1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < G) {
+  if constexpr (row_pipelined<CFG, ROW128>()) {
+    gemm_loop_rows<CFG, OPB_T, P2>(t, ops0, ops1, sc0, sc1, acc);
+  } else {
+    CopyPlan<CFG, OPB_T, ROW128> plan;
+    plan.init(t);
+    if (g0 < G) plan.issue(t, g0, ops0, sc0);  // no groups (an expert without tokens): C = 0
+    // A wave whose rows all lie past the tile's valid rows (the partial last
+    // row tile of an expert or of the matrix) skips its MFMAs and fold; it
+    // still issues its copies and meets every barrier.
+    const int wrow0 = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / CFG::WAVES_N) * CFG::WTM;
+    const bool computes = wrow0 < t.rows;
+    for (int g = g0; g < G; g += 2) {
+      // Group g has landed in stage 0 once this lane's copies are complete;
+      // after the barrier every wave's copies are visible and every wave is
+      // done reading stage 1 (group g-1), which then receives group g+1.
       wait_vmcnt<0>();
       __syncthreads();
-      if (!ILV && g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
+      if (g + 1 < G) plan.issue(t, g + 1, ops1, sc1);
       __builtin_amdgcn_sched_barrier(0);
-      if (computes)
-        compute_group<CFG, OPB_T, ROW128, P2, (OM >= OUT_Q || !P2)>(ops1, sc1, acc, plan, t, ILV && g + 2 < G ? g + 2 : -1, ops0, sc0);
+      if (computes) compute_group<CFG, OPB_T, ROW128, P2>(ops0, sc0, acc);
       __builtin_amdgcn_sched_barrier(0);
+      if (g + 1 < G) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (g + 2 < G) plan.issue(t, g + 2, ops0, sc0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (computes) compute_group<CFG, OPB_T, ROW128, P2>(ops1, sc1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
-
-  if (ILV) wait_vmcnt<0>();  // the last group's (empty) interleaved copies
 
   // ---- epilogue: four consecutive columns per lane, FP32 or (OB) BF16 ----
   const int tid_e = threadIdx.x;
