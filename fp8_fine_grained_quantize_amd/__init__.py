@@ -22,6 +22,7 @@ __all__ = [
     "requantize_128x1_from_1x128", "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled",
     "quantize_128x1_grouped", "token_group_slots", "grouped_wgrad_fp8_blockscaled", "gemm_fp8_blockscaled_q1x128",
     "workspace_bytes", "status_string", "abi_version", "EXPORTED_SYMBOLS", "empty_pitched", "as_pitched",
+    "mfma_probe",
 ]
 
 OP_N, OP_T = 0, 1
@@ -50,6 +51,7 @@ _SIGNATURES = {
     "fp8blk_grouped_wgrad_fp8_blockscaled": (_int, [_i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64,
                                                     _vp, _u32, _vp, _i64, _i64, _vp]),
     "fp8blk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "fp8blk_mfma_probe": (_int, [_int, _vp, _vp, _vp, _vp]),
     "fp8blk_status_string": (ctypes.c_char_p, [_int]),
     "fp8blk_abi_version": (_int, []),
 }
@@ -89,6 +91,17 @@ def abi_version() -> int:
 
 def workspace_bytes(M: int, N: int, K: int, G: int = 1) -> int:
     return lib().fp8blk_workspace_bytes(M, N, K, G)
+
+
+def mfma_probe(A: torch.Tensor, B: torch.Tensor, instr: int = 0) -> torch.Tensor:
+    """One 16x16 tile product over 128 E4M3 k by matrix-core instruction
+    `instr` (see fp8blk_mfma_probe); A, B uint8 [16][128] on the device."""
+    assert A.dtype == torch.uint8 and B.dtype == torch.uint8
+    assert tuple(A.shape) == (16, 128) and tuple(B.shape) == (16, 128)
+    A, B = A.contiguous(), B.contiguous()
+    C = torch.empty(16, 16, dtype=torch.float32, device=A.device)
+    _check(lib().fp8blk_mfma_probe(instr, _ptr(A), _ptr(B), _ptr(C), _stream()), "mfma_probe")
+    return C
 
 
 def _check(code: int, what: str):

@@ -29,7 +29,7 @@ COMMON_FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "diag.hip"]
 
 
 def _compile(src: str) -> str:

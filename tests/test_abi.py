@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fb.abi_version() == 3
+    assert fb.abi_version() == 4
     assert fb.token_group_slots(65536, 256) == 512 + 256
     assert fb.token_group_slots(100, 3) == 3 and fb.token_group_slots(-1, 3) == 0
     assert fb.status_string(0) == "FP8BLK_OK"

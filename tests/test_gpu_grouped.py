@@ -13,7 +13,7 @@ import fp8_fine_grained_quantize_amd as fb
 import oracle
 import synthetic
 from synthetic import bf16_bits
-from tests.gpu_util import e_norm, f32_dev, np_f32, u8_dev
+from tests.gpu_util import e_norm, f32_dev, np_f32, np_u8, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -83,15 +83,69 @@ def test_moe_up_projection_sampled():
         r0, r1 = int(off_np[e]), int(off_np[e + 1])
         if r1 == r0:
             continue
-        # weights: the oracle quantizes the same BF16 draw (copied bit-exact from the device)
+        # weights: the oracle quantizes the same BF16 draw (copied bit-exact
+        # from the device); the GPU-quantized weight must equal it bit for bit
         W = synthetic.expert_weight("up", int(e), device="cuda").cpu()
         qB, sB = oracle.quantize_block128(bf16_bits(W))
+        assert np.array_equal(np_u8(qB_dev[e]), qB), f"expert {e} weight codes"
+        assert np.array_equal(np_f32(sB_dev[e]).view(np.uint32), sB.view(np.uint32)), f"expert {e} weight scales"
         rows = rng.integers(r0, r1, 64)
         cols = rng.integers(0, N, 64)
         Rv = oracle.gemm_blockscaled_entries(qA[r0:r1], sA[:, r0:r1], qB, sB, rows - r0, cols)
         got = C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
         worst = max(worst, float(np.max(np.abs(got - Rv)) / np.max(np.abs(Rv))))
     print(f"[grouped] sampled E_norm={worst:.3e}", flush=True)
+    assert worst <= 1e-3
+
+
+def test_moe_down_projection_sampled():
+    """The down projection at its full shape: 256 experts over the 65,536
+    expert-ordered rows of the top-8 routing, K = 2048 -> N = 7168, the
+    input H [65536][2048] quantized 1x128 (default scales) and every expert's
+    W_down[e] [2048][7168] quantized 128x128 on the GPU into one stacked
+    tensor, one grouped launch.  Checked on the largest and the smallest
+    non-empty expert and six random ones: their weight codes and scales bit
+    for bit against the oracle's quantization of the same BF16 draw, their
+    rows of H likewise, and 64 sampled outputs each against the oracle's
+    exact-partial sums (gate E_norm <= 1e-3 over the samples)."""
+    r = synthetic.moe_routing()
+    off = r["offsets"]
+    off_np = off.numpy().astype(np.int64)
+    Mt = int(off_np[-1])
+    G, K, N = 256, 2048, 7168
+    H = synthetic.moe_grad("h", Mt, device="cuda")
+    qH, sH = fb.quantize_1x128(H)
+    qD = torch.empty(G, K, N, dtype=torch.uint8, device="cuda")
+    sD = torch.empty(G, K // 128, N // 128, dtype=torch.float32, device="cuda")
+    for e in range(G):
+        fb.quantize_block128(synthetic.expert_weight("down", e, device="cuda"), q=qD[e], s=sD[e])
+    offs = off.to(torch.int32).cuda()
+    print(f"[grouped] moe down {Mt}x{N}x{K}, {G} experts", flush=True)
+    C = fb.grouped_gemm_fp8_blockscaled(offs, qH, sH, qD, sD, opB=oracle.OP_N)
+    torch.cuda.synchronize()
+    counts = np.diff(off_np)
+    nonempty = np.flatnonzero(counts > 0)
+    rng = np.random.default_rng(2)
+    picks = [int(np.argmax(counts)), int(nonempty[np.argmin(counts[nonempty])])]
+    picks += [int(e) for e in rng.choice(np.setdiff1d(nonempty, picks), 6, replace=False)]
+    H_cpu = H.cpu()
+    worst = 0.0
+    for e in picks:
+        r0, r1 = int(off_np[e]), int(off_np[e + 1])
+        qHo, sHo = oracle.quantize_1x128(bf16_bits(H_cpu[r0:r1]))
+        assert np.array_equal(np_u8(qH[r0:r1]), qHo), f"expert {e} input codes"
+        assert np.array_equal(np_f32(sH[:, r0:r1]).view(np.uint32), sHo.view(np.uint32)), f"expert {e} input scales"
+        W = synthetic.expert_weight("down", e, device="cuda").cpu()
+        qB, sB = oracle.quantize_block128(bf16_bits(W))
+        assert np.array_equal(np_u8(qD[e]), qB), f"expert {e} weight codes"
+        assert np.array_equal(np_f32(sD[e]).view(np.uint32), sB.view(np.uint32)), f"expert {e} weight scales"
+        rows = rng.integers(r0, r1, 64)
+        cols = rng.integers(0, N, 64)
+        Rv = oracle.gemm_blockscaled_entries(qHo, sHo, qB, sB, rows - r0, cols)
+        got = C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(got - Rv)) / np.max(np.abs(Rv)))
+        print(f"[grouped] down expert {e} rows {r1 - r0} E_norm={err:.3e}", flush=True)
+        worst = max(worst, err)
     assert worst <= 1e-3
 
 

@@ -62,8 +62,7 @@ def test_single_gemm_inputs(pow2):
 def test_dense_fprop_full_size(pow2):
     A, W = synthetic.dense_fprop()
     _check("1x128", A, pow2)
-    if not pow2:
-        _check("block128", W, pow2)
+    _check("block128", W, pow2)
 
 
 def test_backward_full_size():
