@@ -987,9 +987,10 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
   // (Only FP32-output kernels are split: a split GEMM writes FP32 partials
   // and the reduction writes BF16 when asked to.)
   const int split = blockIdx.y;
-  if (gridDim.y > 1) {
-    C = partials + (int64_t)split * M * N;
-    ldc = N;
+  if (gridDim.y > 1) {  // partial slices of pitch N rounded up to 4 floats (16-byte rows)
+    const int64_t Np = (N + 3) & ~int64_t(3);
+    C = partials + (int64_t)split * M * Np;
+    ldc = Np;
   }
   const int64_t m0 = tm * CFG::BM;
   TileArgs t;
@@ -1150,31 +1151,25 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __rest
 }
 
 // Split-K reduction: C[m][n] = sum over s = 0 .. S-1, in that order, of the
-// partial products partials[s][m][n] (FP32 additions).  Four consecutive
-// columns per thread.
+// partial products partials[s][m][n] (FP32 additions).  The partial slices
+// have row pitch Np = N rounded up to 4 floats, so every thread reads four
+// consecutive columns as 16-byte words (columns from N to Np are padding,
+// read but never stored).
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ partials, int S, int64_t M,
                                                        int64_t N, void* __restrict__ Cv, int64_t ldc, int out_bf16) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index of a 4-column chunk
-  const int64_t cpr = (N + 3) / 4;
+  const int64_t Np = (N + 3) & ~int64_t(3);
+  const int64_t cpr = Np / 4;
   const int64_t m = q / cpr, n = (q % cpr) * 4;
   if (m >= M) return;
-  const int64_t MN = M * N;
-  const float* src = partials + m * N + n;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (n + 4 <= N && (N & 3) == 0) {
-    float4 a = *reinterpret_cast<const float4*>(src);
-    for (int s = 1; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(src + s * MN);
-      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-    }
-    acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
-  } else {
-    for (int r = 0; r < 4 && n + r < N; ++r) {
-      float a = src[r];
-      for (int s = 1; s < S; ++s) a += src[s * MN + r];
-      acc[r] = a;
-    }
+  const int64_t MN = M * Np;
+  const float* src = partials + m * Np + n;
+  float4 a = *reinterpret_cast<const float4*>(src);
+  for (int s = 1; s < S; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(src + s * MN);
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
   }
+  const float acc[4] = {a.x, a.y, a.z, a.w};
   if (out_bf16) {
     uint16_t* dst = static_cast<uint16_t*>(Cv) + m * ldc + n;
     if (n + 4 <= N)
@@ -1207,7 +1202,8 @@ static int64_t splitk_count(int64_t M, int64_t N, int64_t K) {
 
 static size_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t S = splitk_count(M, N, K);
-  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+  const int64_t Np = (N + 3) & ~int64_t(3);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)Np * sizeof(float) : 0;
 }
 
 template <class CFG, bool OPB_T, bool ROW128, bool P2>
@@ -1229,7 +1225,7 @@ static fp8blk_status_t launch_dense(int64_t M, int64_t N, int64_t K, const uint8
                        nullptr);
   if (S > 1) {
     if (hipGetLastError() != hipSuccess) return FP8BLK_ERR_LAUNCH;
-    const int64_t chunks = M * ceil_div(N, 4);
+    const int64_t chunks = M * ceil_div(N, 4);  // N rounded up to 4 floats, in chunks of 4
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(chunks, 256)), dim3(256), 0, stream, partials, (int)S,
                        M, N, C, ldc, out_bf16);
   }
@@ -1263,10 +1259,13 @@ extern "C" size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_
   return splitk_bytes(M, N, K);
 }
 
-extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
-                                                       const float* sA, const uint8_t* B, int64_t ldb, int opB,
-                                                       const float* sB, int bscale_mode, void* C, int64_t ldc,
-                                                       void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks and tile/split choice shared by the dense entry points.
+// `workspace` is the split-K partials buffer (S slices of M x N rounded up
+// to 4 floats); with too small a workspace the GEMM runs in one pass, or,
+// with `strict`, the call fails with FP8BLK_ERR_UNSUPPORTED.
+static fp8blk_status_t gemm_dense(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const float* sA,
+                                  const uint8_t* B, int64_t ldb, int opB, const float* sB, int bscale_mode, void* C,
+                                  int64_t ldc, void* workspace, size_t workspace_bytes, bool strict, void* stream) {
   if (M < 0 || N < 0 || K < 0) return FP8BLK_ERR_INVALID_ARG;
   const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
   const int ob = (opB & FP8BLK_GEMM_OUT_BF16) != 0;
@@ -1299,6 +1298,8 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
   if (S > 1) {
     if (workspace != nullptr && workspace_bytes >= splitk_bytes(M, N, K) && aligned(workspace, 16))
       partials = static_cast<float*>(workspace);
+    else if (strict)
+      return FP8BLK_ERR_UNSUPPORTED;
     else
       S = 1;
   }
@@ -1314,6 +1315,14 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
   if (big_tiles >= 128)
     return dispatch_dense<BigCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   return dispatch_dense<SmallCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
+}
+
+extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                                       const float* sA, const uint8_t* B, int64_t ldb, int opB,
+                                                       const float* sB, int bscale_mode, void* C, int64_t ldc,
+                                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_dense(M, N, K, A, lda, sA, B, ldb, opB, sB, bscale_mode, C, ldc, workspace, workspace_bytes, false,
+                    stream);
 }
 
 // Dense GEMM with the output quantized on store (1x128 tiles along each row

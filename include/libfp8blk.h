@@ -29,7 +29,9 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) on
  *     the current HIP device.  The caller owns every buffer; the library never
- *     allocates, frees or synchronizes, and keeps no state between calls.
+ *     allocates, frees or synchronizes.  Between calls it keeps only one
+ *     per-device lookup, made once and thread-safe: the device's
+ *     compute-unit count (which sets the split-K choice).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     All work is enqueued asynchronously on it.
  *   - BF16 inputs are raw bit patterns (uint16_t).  Matrices are row-major
