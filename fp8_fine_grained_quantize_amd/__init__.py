@@ -22,7 +22,7 @@ __all__ = [
     "requantize_128x1_from_1x128", "gemm_fp8_blockscaled", "grouped_gemm_fp8_blockscaled",
     "quantize_128x1_grouped", "token_group_slots", "grouped_wgrad_fp8_blockscaled", "gemm_fp8_blockscaled_q1x128",
     "workspace_bytes", "status_string", "abi_version", "EXPORTED_SYMBOLS", "empty_pitched", "as_pitched",
-    "mfma_probe",
+    "mfma_probe", "gemm_fp8_blockscaled_noalloc",
 ]
 
 OP_N, OP_T = 0, 1
@@ -52,6 +52,8 @@ _SIGNATURES = {
                                                     _vp, _u32, _vp, _i64, _i64, _vp]),
     "fp8blk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "fp8blk_mfma_probe": (_int, [_int, _vp, _vp, _vp, _vp]),
+    "fp8blk_gemm_fp8_blockscaled_noalloc": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _vp, _int,
+                                                   _vp, _i64, _vp]),
     "fp8blk_status_string": (ctypes.c_char_p, [_int]),
     "fp8blk_abi_version": (_int, []),
 }
@@ -245,6 +247,21 @@ def gemm_fp8_blockscaled(A, sA, B, sB, opB: int = OP_N, bscale_mode: int = BSCAL
                                              opB | (GEMM_POW2_SCALES if pow2_scales else 0) | ob, _ptr(sB), bscale_mode,
                                              _ptr(C), _pitch(C), ws_ptr, ws_bytes, _stream()),
            "gemm_fp8_blockscaled")
+    return C
+
+
+def gemm_fp8_blockscaled_noalloc(A, sA, B, sB, C, opB: int = OP_N, bscale_mode: int = BSCALE_BLOCK128,
+                                 pow2_scales: bool = False):
+    """The dense GEMM through fp8blk_gemm_fp8_blockscaled_noalloc: C (float32
+    or bfloat16) given by the caller; split-K partials in the library's own
+    per-device scratch array, so the call allocates nothing."""
+    M, K = A.shape
+    N = B.shape[1] if opB == OP_N else B.shape[0]
+    ob, _, _ = _out_flag(C, C.dtype)
+    _check(lib().fp8blk_gemm_fp8_blockscaled_noalloc(M, N, K, _ptr(A), _pitch(A), _ptr(sA), _ptr(B), _pitch(B),
+                                                     opB | (GEMM_POW2_SCALES if pow2_scales else 0) | ob, _ptr(sB),
+                                                     bscale_mode, _ptr(C), _pitch(C), _stream()),
+           "gemm_fp8_blockscaled_noalloc")
     return C
 
 

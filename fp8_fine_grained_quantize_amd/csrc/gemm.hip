@@ -35,6 +35,9 @@
 //   MFMA operand layout (16x16x128, FP8): lane l holds row/column l%16 and
 //   k = 32*(l/16) .. 32*(l/16)+31; result lane l holds rows 4*(l/16)+i,
 //   column l%16.
+#include <atomic>
+#include <mutex>
+
 #include "fp8_device.h"
 #include "host_common.h"
 #include "token_groups.h"
@@ -1323,6 +1326,50 @@ extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int
                                                        void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_dense(M, N, K, A, lda, sA, B, ldb, opB, sB, bscale_mode, C, ldc, workspace, workspace_bytes, false,
                     stream);
+}
+
+// ---- The same GEMM without any allocation --------------------------------
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid it): the split-K partials live in `scratch`, a
+// file-scope device array of FP8BLK_NOALLOC_SCRATCH_BYTES that each GPU holds
+// for the life of the process.  Its device address is looked up once per
+// device (hipGetSymbolAddress with that device current) and kept; host code
+// passes only that address to the kernels, never the array's name.
+static __device__ __align__(256) float scratch[FP8BLK_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+static float* scratch_on_current_device() {
+  static std::mutex mu;
+  static std::atomic<float*> ptrs[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  float* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = ptrs[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    p = static_cast<float*>(q);
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+extern "C" fp8blk_status_t fp8blk_gemm_fp8_blockscaled_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                                               int64_t lda, const float* sA, const uint8_t* B,
+                                                               int64_t ldb, int opB, const float* sB, int bscale_mode,
+                                                               void* C, int64_t ldc, void* stream) {
+  // Shapes whose partials would not fit are rejected before anything is
+  // looked up or enqueued (the split count is the workspace entry point's).
+  if (M > 0 && N > 0 && K > 0 && K % 128 == 0 && splitk_bytes(M, N, K) > FP8BLK_NOALLOC_SCRATCH_BYTES)
+    return FP8BLK_ERR_UNSUPPORTED;
+  float* ws = nullptr;
+  if (M > 0 && N > 0 && K > 0 && K % 128 == 0 && splitk_bytes(M, N, K) > 0) {
+    ws = scratch_on_current_device();
+    if (ws == nullptr) return FP8BLK_ERR_LAUNCH;
+  }
+  return gemm_dense(M, N, K, A, lda, sA, B, ldb, opB, sB, bscale_mode, C, ldc, ws,
+                    ws != nullptr ? (size_t)FP8BLK_NOALLOC_SCRATCH_BYTES : 0, true, stream);
 }
 
 // Dense GEMM with the output quantized on store (1x128 tiles along each row

@@ -29,9 +29,10 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) on
  *     the current HIP device.  The caller owns every buffer; the library never
- *     allocates, frees or synchronizes.  Between calls it keeps only one
- *     per-device lookup, made once and thread-safe: the device's
- *     compute-unit count (which sets the split-K choice).
+ *     allocates, frees or synchronizes.  Between calls it keeps only two
+ *     per-device lookups, each made once and thread-safe: the device's
+ *     compute-unit count (which sets the split-K choice) and, for
+ *     fp8blk_gemm_fp8_blockscaled_noalloc, the address of its scratch array.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     All work is enqueued asynchronously on it.
  *   - BF16 inputs are raw bit patterns (uint16_t).  Matrices are row-major
@@ -186,6 +187,26 @@ fp8blk_status_t fp8blk_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                             void* C, int64_t ldc,
                                             void* workspace, size_t workspace_bytes,
                                             void* stream);
+
+/*
+ * The same GEMM for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): identical
+ * arguments and results to fp8blk_gemm_fp8_blockscaled given a large enough
+ * workspace, with the split-K partials in a device array that the library
+ * holds on each GPU for the life of the process
+ * (FP8BLK_NOALLOC_SCRATCH_BYTES).  It calls no allocating routine; its first
+ * call on a device looks the array's address up once.  Shapes whose
+ * partials exceed the array return FP8BLK_ERR_UNSUPPORTED before anything is
+ * enqueued (with 256 compute units no valid shape does).  Every call on one
+ * GPU uses the same array: calls that overlap on one GPU (other streams,
+ * other threads) race and give wrong results.
+ */
+#define FP8BLK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fp8blk_status_t fp8blk_gemm_fp8_blockscaled_noalloc(int64_t M, int64_t N, int64_t K,
+                                                    const uint8_t* A, int64_t lda, const float* sA,
+                                                    const uint8_t* B, int64_t ldb, int opB,
+                                                    const float* sB, int bscale_mode,
+                                                    void* C, int64_t ldc, void* stream);
 
 /*
  * The same GEMM with its output quantized on store for the next layer's
