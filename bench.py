@@ -290,6 +290,13 @@ def main():
             for j in range(S):
                 fb.quantize_1x128(A[j], pow2=p2, q=qA[j], s=sA[j])
                 fb.quantize_block128(W[j], pow2=p2, q=qW[j], s=sW[j])
+            # the FP32-output GEMM timed back to back like the BF16 and fused
+            # variants below (the headline figure above times it inside the step)
+            t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qA[i % S], sA[i % S], qW[i % S], sW[i % S],
+                                                                      C=C[i % S], pow2_scales=p2), 40)
+            extras["fprop_gemm_fp32_out_back_to_back" + ("_pow2_scales" if p2 else "")] = {
+                "us": round(t * 1e3, 2), "TFLOP/s": round(flops / t / 1e9, 1),
+                "frac_mfma": round(flops / t / 1e9 / FP8_PEAK_TFLOPS, 4)}
             t = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qA[i % S], sA[i % S], qW[i % S], sW[i % S],
                                                                       C=Cb[i % S], pow2_scales=p2), 40)
             extras["fprop_gemm_bf16_out" + ("_pow2_scales" if p2 else "")] = {
@@ -362,6 +369,22 @@ def run_extras(torch, fb, synthetic, dev, np):
     res["launch_floor"] = {
         "quantize_1x128_1x128_us": round(timed_events(torch, lambda i: fb.quantize_1x128(x1, q=q1, s=s1), 40) * 1e3, 2),
         "gemm_128x128x128_us": round(timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(a1, sa1, b1, sb1, C=c1), 40) * 1e3, 2)}
+    # the single-GEMM workload (256x512x1024, FP32 out): its three kernels
+    A1, B1 = synthetic.single_gemm()
+    A1d, B1d = A1.to(dev), B1.to(dev)
+    qa1, sa1_ = fb.quantize_1x128(A1d)
+    qb1, sb1_ = fb.quantize_block128(B1d)
+    c1g = torch.empty(256, 512, dtype=torch.float32, device=dev)
+    t_qa = timed_events(torch, lambda i: fb.quantize_1x128(A1d, q=qa1, s=sa1_), 40)
+    t_qb = timed_events(torch, lambda i: fb.quantize_block128(B1d, q=qb1, s=sb1_), 40)
+    t_g1 = timed_events(torch, lambda i: fb.gemm_fp8_blockscaled(qa1, sa1_, qb1, sb1_, C=c1g), 40)
+    fl1 = 2.0 * 256 * 512 * 1024
+    res["single_gemm_256x512x1024"] = {
+        "quantize_1x128_us": round(t_qa * 1e3, 2), "quantize_block128_us": round(t_qb * 1e3, 2),
+        "gemm_us": round(t_g1 * 1e3, 2), "gemm_TFLOP/s": round(fl1 / t_g1 / 1e9, 2),
+        "gemm_frac_mfma": round(fl1 / t_g1 / 1e9 / FP8_PEAK_TFLOPS, 5),
+        "note": "launch-latency bound (0.27 GFLOP); compare launch_floor"}
+    del A1d, B1d, qa1, sa1_, qb1, sb1_, c1g
     # backward: Dgrad dX = dY W^T (OP_T), Wgrad dW = X^T dY (128x1 operands, ROW128)
     X, W, dY = synthetic.backward()
     Xd, Wd, dYd = X.to(dev), W.to(dev), dY.to(dev)
@@ -394,7 +417,8 @@ def run_extras(torch, fb, synthetic, dev, np):
     # read and write from HBM, not from the Infinity Cache.
     for name, x, fn, bpe in [("quantize_128x1_X", Xd, fb.quantize_128x1, QUANT_BYTES_1X128),
                              ("quantize_128x1_dY", dYd, fb.quantize_128x1, QUANT_BYTES_1X128),
-                             ("quantize_1x128_dY", dYd, fb.quantize_1x128, QUANT_BYTES_1X128)]:
+                             ("quantize_1x128_dY", dYd, fb.quantize_1x128, QUANT_BYTES_1X128),
+                             ("quantize_block128_W_7168x2048", Wd, fb.quantize_block128, QUANT_BYTES_BLOCK)]:
         ns = n_sets(x.numel() * bpe)
         sets = [(x.clone(), *fn(x)) for _ in range(ns)]
         t = timed_events(torch, lambda i: fn(sets[i % ns][0], q=sets[i % ns][1], s=sets[i % ns][2])
@@ -447,10 +471,21 @@ def run_extras(torch, fb, synthetic, dev, np):
     qA = qX[tok].contiguous()
     sA = sX[:, tok].contiguous()
     Mt = qA.shape[0]
+    # All 256 experts' weights quantized 128x128 in one launch on the stacked
+    # [256*K][N] tensor (K a multiple of 128: the same blocks as each expert's
+    # own quantization, scales [256*K/128][N/128] = the per-expert tables back
+    # to back), timed as its own leg.
+    Wst = torch.empty(G * Kh, Nu, dtype=torch.bfloat16, device=dev)
+    for e in range(G):
+        Wst[e * Kh:(e + 1) * Kh] = synthetic.expert_weight("up", e, device=dev)
     qU = torch.empty(G, Kh, Nu, dtype=torch.uint8, device=dev)
     sU = torch.empty(G, Kh // 128, Nu // 128, dtype=torch.float32, device=dev)
-    for e in range(G):
-        fb.quantize_block128(synthetic.expert_weight("up", e, device=dev), q=qU[e], s=sU[e])
+    qU2, sU2 = qU.view(G * Kh, Nu), sU.view(G * Kh // 128, Nu // 128)
+    t = timed_events(torch, lambda i: fb.quantize_block128(Wst, q=qU2, s=sU2), 3)
+    byts = G * Kh * Nu * QUANT_BYTES_BLOCK
+    res["quantize_block128_moe_up_weights_256x7168x4096"] = {
+        "us": round(t * 1e3, 1), "GB/s": round(byts / t / 1e6, 1), "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4),
+        "blocks": G * (Kh // 128) * (Nu // 128)}
     Cu = torch.empty(Mt, Nu, dtype=torch.float32, device=dev)
     t = timed_events(torch, lambda i: fb.grouped_gemm_fp8_blockscaled(offs, qA, sA, qU, sU, C=Cu), 3)
     fl = 2.0 * Mt * Nu * Kh
@@ -462,8 +497,8 @@ def run_extras(torch, fb, synthetic, dev, np):
     # The up projection with power-of-two weight scales too (its input is the
     # pages' power-of-two activation), the scales then applied by the MFMA.
     Cu2 = torch.empty(Mt, Nu, dtype=torch.float32, device=dev)
-    for e in range(G):
-        fb.quantize_block128(synthetic.expert_weight("up", e, device=dev), pow2=True, q=qU[e], s=sU[e])
+    fb.quantize_block128(Wst, pow2=True, q=qU2, s=sU2)
+    del Wst
     t = timed_events(torch, lambda i: fb.grouped_gemm_fp8_blockscaled(offs, qA, sA, qU, sU, C=Cu2, pow2_scales=True), 3)
     res["grouped_up_gate_65536x4096x7168_E256_pow2_scales"] = {"us": round(t * 1e3, 1),
                                                                "TFLOP/s": round(fl / t / 1e9, 1),
@@ -473,10 +508,26 @@ def run_extras(torch, fb, synthetic, dev, np):
     H = (torch.nn.functional.silu(Cu[:, :2048]) * Cu[:, 2048:]).to(torch.bfloat16)
     del Cu
     qH, sH = fb.quantize_1x128(H)
+    ns = n_sets(H.numel() * QUANT_BYTES_1X128)
+    sets = [(H, qH, sH)] + [(H.clone(), *fb.quantize_1x128(H)) for _ in range(ns - 1)]
+    t = timed_events(torch, lambda i: fb.quantize_1x128(sets[i % ns][0], q=sets[i % ns][1], s=sets[i % ns][2]),
+                     max(reps, 2 * ns))
+    del sets
+    byts = H.numel() * QUANT_BYTES_1X128
+    res["quantize_1x128_moe_H_65536x2048"] = {"us": round(t * 1e3, 2), "GB/s": round(byts / t / 1e6, 1),
+                                              "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4), "sets": ns}
+    Wst = torch.empty(G * 2048, Nd, dtype=torch.bfloat16, device=dev)
+    for e in range(G):
+        Wst[e * 2048:(e + 1) * 2048] = synthetic.expert_weight("down", e, device=dev)
     qD = torch.empty(G, 2048, Nd, dtype=torch.uint8, device=dev)
     sD = torch.empty(G, 2048 // 128, Nd // 128, dtype=torch.float32, device=dev)
-    for e in range(G):
-        fb.quantize_block128(synthetic.expert_weight("down", e, device=dev), q=qD[e], s=sD[e])
+    qD2, sD2 = qD.view(G * 2048, Nd), sD.view(G * 2048 // 128, Nd // 128)
+    t = timed_events(torch, lambda i: fb.quantize_block128(Wst, q=qD2, s=sD2), 3)
+    byts = G * 2048 * Nd * QUANT_BYTES_BLOCK
+    res["quantize_block128_moe_down_weights_256x2048x7168"] = {
+        "us": round(t * 1e3, 1), "GB/s": round(byts / t / 1e6, 1), "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4),
+        "blocks": G * (2048 // 128) * (Nd // 128)}
+    del Wst
     Cdn = torch.empty(Mt, Nd, dtype=torch.float32, device=dev)
     t = timed_events(torch, lambda i: fb.grouped_gemm_fp8_blockscaled(offs, qH, sH, qD, sD, C=Cdn), 3)
     fl = 2.0 * Mt * Nd * 2048

@@ -170,12 +170,13 @@ __device__ __forceinline__ void dma4(v4i r, uint32_t voff, uint8_t* lds_base) {
                : "memory", "m0");
 }
 
-// BF16 bits of an FP32 value, rounded to nearest even (a NaN stays a quiet
-// NaN; values beyond the largest finite BF16 round to infinity).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two FP32 values rounded to BF16 (nearest even; subnormals kept; values
+// beyond the largest finite BF16 become infinities; a NaN stays a NaN),
+// packed: `lo` in bits 15:0, `hi` in bits 31:16.  One v_cvt_pk_bf16_f32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // 4 x 4 transpose between the four 16-lane rows of a wave and four
@@ -819,6 +820,19 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     // the partner wave's through LDS (the stage buffer is free once every
     // wave has left the K loop).
     uint32_t* red = reinterpret_cast<uint32_t*>(ops0);
+    // The results rounded to BF16 in place (a BF16 value is the upper half
+    // of its FP32 word).
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint32_t p01 = bf16_pack(acc[i][j][0], acc[i][j][1]);
+        const uint32_t p23 = bf16_pack(acc[i][j][2], acc[i][j][3]);
+        acc[i][j][0] = __uint_as_float(p01 << 16);
+        acc[i][j][1] = __uint_as_float(p01 & 0xFFFF0000u);
+        acc[i][j][2] = __uint_as_float(p23 << 16);
+        acc[i][j][3] = __uint_as_float(p23 & 0xFFFF0000u);
+      }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -828,7 +842,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
         const int64_t col = t.n0 + wn_e * CFG::WTN + 16 * j + 4 * lq_e;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (col + r < t.N) m = max(m, bf16_rne(acc[i][j][r]) & 0x7FFFu);
+          if (col + r < t.N) m = max(m, (__float_as_uint(acc[i][j][r]) >> 16) & 0x7FFFu);
       }
       m = max(m, (uint32_t)__shfl_xor((int)m, 16));
       m = max(m, (uint32_t)__shfl_xor((int)m, 32));
@@ -853,7 +867,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
         float y[4], xv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          xv[r] = __uint_as_float(bf16_rne(acc[i][j][r]) << 16);
+          xv[r] = acc[i][j][r];
           y[r] = quotient_fast<QP2, true>(xv[r], ts);
         }
         if (__builtin_expect(ts.slow, 0)) {
@@ -888,8 +902,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
       uint32_t lo[TN], hi[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        lo[j] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-        hi[j] = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        lo[j] = bf16_pack(acc[i][j][0], acc[i][j][1]);
+        hi[j] = bf16_pack(acc[i][j][2], acc[i][j][3]);
       }
       transpose_rows4(lo);
       transpose_rows4(hi);
@@ -1176,10 +1190,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   if (out_bf16) {
     uint16_t* dst = static_cast<uint16_t*>(Cv) + m * ldc + n;
     if (n + 4 <= N)
-      *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16),
-                                                  bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16));
+      *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_pack(acc[0], acc[1]), bf16_pack(acc[2], acc[3]));
     else
-      for (int r = 0; r < 4 && n + r < N; ++r) dst[r] = (uint16_t)bf16_rne(acc[r]);
+      for (int r = 0; r < 4 && n + r < N; ++r) dst[r] = (uint16_t)(bf16_pack(acc[r], 0.0f) & 0xFFFFu);
   } else {
     float* dst = static_cast<float*>(Cv) + m * ldc + n;
     if (n + 4 <= N)
@@ -1190,16 +1203,28 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }
 
 // K splits for a dense GEMM: only when its 128 x 128 tiles cannot fill the
-// compute units; each split keeps at least four K groups.
+// compute units and K is long enough (at least FP8BLK_SPLITK_MIN_GROUPS
+// groups) for the split to save more than the reduction's launch costs; each
+// split keeps at least eight K groups, at most FP8BLK_SPLITK_MAX splits.
+// Measured on 1024 x 1024 x K (one box): K = 4096 with 2 / 4 / 8 splits
+// 27.6 / 22.0 / 24.4 us, K = 8192 40.7 / 28.8 / 28.9 us, K = 16384
+// 70.7 / 44.7 / 38.9 us.
+#ifndef FP8BLK_SPLITK_MIN_GROUPS
+#define FP8BLK_SPLITK_MIN_GROUPS 16
+#endif
+#ifndef FP8BLK_SPLITK_MAX
+#define FP8BLK_SPLITK_MAX 16
+#endif
 static int64_t splitk_count(int64_t M, int64_t N, int64_t K) {
   const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
   if (big_tiles >= 128) return 1;
+  const int64_t G = K / 128;
+  if (G < FP8BLK_SPLITK_MIN_GROUPS) return 1;
   const int64_t tiles = ceil_div(M, SmallCfg::BM) * ceil_div(N, SmallCfg::BN);
   const int64_t slots = 2 * (int64_t)device_cus();  // two 128 x 128 workgroups fit per CU
   int64_t S = ceil_div(slots, tiles);
-  const int64_t G = K / 128;
-  if (S > G / 4) S = G / 4;
-  if (S > 16) S = 16;
+  if (S > G / 8) S = G / 8;
+  if (S > FP8BLK_SPLITK_MAX) S = FP8BLK_SPLITK_MAX;
   return S < 1 ? 1 : S;
 }
 
@@ -1435,10 +1460,14 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
     void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  // 128 x 128 tiles: expert row counts are small and skewed (mean 256 rows
-  // for 256 experts, top-8 of 8192 tokens), and a 128-row tile pads the
-  // experts' row ranges about half as much as a 256-row tile does.
-  using CFG = SmallCfg;
+  // 256 x 256 tiles on the row-pipelined loop.  With 256 experts of mean
+  // 256 rows (skewed), 256-row tiles pad the experts' row ranges more than
+  // 128-row tiles (64 % against 79 % useful rows), but each group's copies
+  // feed four times the MFMA work, and the copies, not the matrix cores,
+  // bound these kernels: measured against 128 x 128 tiles (interleaved, one
+  // box, bitwise identical) MoE up 3.32 / 3.50 ms, down 2.08 / 2.16 ms, down
+  // Dgrad 1.72 / 1.71 ms.
+  using CFG = BigCfg;
   if (G < 0 || M_total < 0 || N < 0 || K < 0 || max_group_rows < 0) return FP8BLK_ERR_INVALID_ARG;
   const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
   const int ob = (opB & FP8BLK_GEMM_OUT_BF16) != 0;

@@ -83,23 +83,43 @@ def test_block128_past_2g_elements():
 @pytest.mark.parametrize("pow2", [False, True])
 def test_block128_one_wave_per_block(pow2):
     """Above 6144 blocks quantize_block128 takes one wave per block; ragged
-    row and column edges, outlier columns, both scale modes."""
-    R, C = 10000, 10016
-    assert (-(-R // 128)) * (-(-C // 128)) > 6144
+    row and column edges (10013 columns: the last block's rows end 1-7
+    elements into a 16-byte chunk), a pitched view, outlier columns, both
+    scale modes; every code and scale against the oracle."""
+    R, C = 10000, 10013
+    assert (-(-R // 128)) * (-(-C // 128)) > 6144 and C % 8 != 0
     print(f"[max] quantize_block128 one wave per block [{R}][{C}] pow2={pow2}", flush=True)
     g = torch.Generator().manual_seed(31)
-    x = synthetic.randn_bf16((R, C), 1.0, g, outlier_cols=3, outlier_factor=60.0).cuda()
+    x_cpu = synthetic.randn_bf16((R, C), 1.0, g, outlier_cols=3, outlier_factor=60.0)
+    x = fb.as_pitched(x_cpu.cuda())
     q, s = fb.quantize_block128(x, pow2=pow2)
     torch.cuda.synchronize()
-    GR, GC = -(-R // 128), -(-C // 128)
-    rng = np.random.default_rng(3)
-    picks = [(0, 0), (0, GC - 1), (GR - 1, 0), (GR - 1, GC - 1)] + [tuple(v) for v in rng.integers(0, [GR, GC], (8, 2))]
-    for bi, bj in picks:
-        rs, cs = slice(128 * bi, min(R, 128 * bi + 128)), slice(128 * bj, min(C, 128 * bj + 128))
-        qo, so = oracle.quantize_block128(bf16_bits(x[rs, cs].cpu()), pow2=pow2)
-        assert np.array_equal(np_u8(q[rs, cs]), qo), (bi, bj)
-        assert np_f32(s[bi, bj]).view(np.uint32) == so[0, 0].view(np.uint32), (bi, bj)
+    qo, so = oracle.quantize_block128(bf16_bits(x_cpu), pow2=pow2)
+    assert np.array_equal(np_u8(q), qo)
+    assert np.array_equal(np_f32(s).view(np.uint32), so.view(np.uint32))
     del x, q, s
+    _free()
+
+
+def test_block128_stacked_expert_weights():
+    """The 256 down-projection weights of the MoE workload quantized in one
+    launch on their stacked [256*2048][7168] tensor (57344 blocks, the
+    one-wave kernel) equal each expert's own quantization: 2048 is a multiple
+    of 128, so the block grids coincide and the stacked scales are the
+    per-expert tables back to back.  Checked against the oracle on four
+    experts (first, last, two others)."""
+    G, K, N = 256, 2048, 7168
+    W = torch.empty(G * K, N, dtype=torch.bfloat16, device="cuda")
+    for e in range(G):
+        W[e * K:(e + 1) * K] = synthetic.expert_weight("down", e, device="cuda")
+    print(f"[max] quantize_block128 stacked expert weights [{G * K}][{N}]", flush=True)
+    q, s = fb.quantize_block128(W)
+    torch.cuda.synchronize()
+    for e in (0, 97, 200, G - 1):
+        qo, so = oracle.quantize_block128(bf16_bits(W[e * K:(e + 1) * K].cpu()))
+        assert np.array_equal(np_u8(q[e * K:(e + 1) * K]), qo), e
+        assert np.array_equal(np_f32(s[e * (K // 128):(e + 1) * (K // 128)]).view(np.uint32), so.view(np.uint32)), e
+    del W, q, s
     _free()
 
 
