@@ -349,7 +349,7 @@ struct CopyPlan {
 #define FP8BLK_ROWPIPE_MIN_TM 8
 #endif
 template <class CFG, bool ROW128>
-constexpr bool row_pipelined() { return CFG::TM >= FP8BLK_ROWPIPE_MIN_TM && !ROW128; }
+constexpr bool row_pipelined() { return CFG::TM >= FP8BLK_ROWPIPE_MIN_TM; }
 
 // One K group of MFMAs and scale folds on operands already in LDS (`ops`:
 // A tile then B tile; `sc`: row scales in lane order, then column/block
@@ -542,7 +542,7 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
 
 // Copy resources of the next K group: A tile, B tile and this wave's scale
 // run, each a 64-bit address advanced by a fixed stride per group.
-template <class CFG, bool OPB_T>
+template <class CFG, bool OPB_T, bool ROW128>
 struct GroupCursor {
   uint64_t a, b, s;
   int64_t b_step, s_step;
@@ -568,6 +568,10 @@ struct GroupCursor {
       s = reinterpret_cast<uint64_t>(t.sA + (int64_t)g * t.sA_ld);
       s_step = t.sA_ld * 4;
       s_cnt = (int32_t)(t.rows * 4);
+    } else if (ROW128) {  // column scales [K/128][N]: the tile's BN columns of group g
+      s = reinterpret_cast<uint64_t>(t.sB + (int64_t)g * t.sB_ld + t.n0);
+      s_step = t.sB_ld * 4;
+      s_cnt = (int32_t)((t.N - t.n0) * 4);
     } else if (OPB_T) {
       s = reinterpret_cast<uint64_t>(t.sB + nb0 * Gk + g);
       s_step = 4;
@@ -595,11 +599,11 @@ struct GroupCursor {
 };
 
 // Copies n0 .. n1-1 of a group (A blocks, then B blocks, then the scale run).
-template <class CFG, bool OPB_T>
-__device__ __forceinline__ void issue_copies(const TileArgs& t, const CopyPlan<CFG, OPB_T, false>& plan,
+template <class CFG, bool OPB_T, bool ROW128>
+__device__ __forceinline__ void issue_copies(const TileArgs& t, const CopyPlan<CFG, OPB_T, ROW128>& plan,
                                              uint32_t scoff, const v4i& ra, const v4i& rb, const v4i& rs, int n0,
                                              int n1, uint8_t* buf, float* sbuf, int wave, int blk) {
-  constexpr int NW = CFG::NW, KSTEP = CopyPlan<CFG, OPB_T, false>::KSTEP;
+  constexpr int NW = CFG::NW, KSTEP = CopyPlan<CFG, OPB_T, ROW128>::KSTEP;
 #pragma unroll
   for (int n = n0; n < n1; ++n) {
     if (n < CFG::A_ITERS) {
@@ -616,13 +620,13 @@ __device__ __forceinline__ void issue_copies(const TileArgs& t, const CopyPlan<C
 
 // One K group of a row-pipelined tile: operands of this group in `ops`/`sc`,
 // the next group's copies (resources ra/rb/rs) into `nops`/`nsc`.
-template <class CFG, bool OPB_T, bool P2>
+template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void compute_group_rows(const uint8_t* ops, const float* sc, v4f (&acc)[CFG::TM][CFG::TN],
-                                                   const TileArgs& t, const CopyPlan<CFG, OPB_T, false>& plan,
+                                                   const TileArgs& t, const CopyPlan<CFG, OPB_T, ROW128>& plan,
                                                    uint32_t scoff, const v4i& ra, const v4i& rb, const v4i& rs,
                                                    uint8_t* nops, float* nsc, int wave, int blk) {
   constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN, R = FP8BLK_FOLD_RING;
-  constexpr int LOADS = CopyPlan<CFG, OPB_T, false>::LOADS, CR = FP8BLK_COPY_ROWS;
+  constexpr int LOADS = CopyPlan<CFG, OPB_T, ROW128>::LOADS, CR = FP8BLK_COPY_ROWS;
   static_assert(CR >= 1 && CR <= TM, "copy rows");
   const int lane = threadIdx.x & 63;
   const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
@@ -656,51 +660,78 @@ __device__ __forceinline__ void compute_group_rows(const uint8_t* ops, const flo
       bfr[j] = v8i{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
     }
   }
-  // Row scales of this lane's row tiles and the wave's block scale.
+  // Row scales of this lane's row tiles, and the wave's block scale or (ROW128)
+  // the column scales of its column tiles.
   float sa[TM];
 #pragma unroll
   for (int i = 0; i < TM; i += 4) {
     const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
     sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
   }
-  const float sbb = sc[BM + (wn * CFG::WTN) / 128];
+  float sbb = 0.0f;
+  float4 sbv[ROW128 ? TN : 1];
+  if constexpr (ROW128) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sc + BM + wn * CFG::WTN + 16 * j + 4 * lq);
+  } else {
+    sbb = sc[BM + (wn * CFG::WTN) / 128];
+  }
 
   if constexpr (P2) {
-    // E8M0 exponents: row tile i in byte i%4 of sae[i/4]; the block scale.
+    // E8M0 exponents: row tile i in byte i%4 of sae[i/4]; the block scale,
+    // or (ROW128) column tile j's column l16 in byte j of sbe.
+    static_assert(!ROW128 || TN <= 4, "four column tiles per packed scale register");
     uint32_t sae[(TM + 3) / 4];
 #pragma unroll
     for (int q = 0; q < (TM + 3) / 4; ++q) sae[q] = 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) sae[i / 4] |= e8m0_of(sa[i]) << (8 * (i % 4));
-    const uint32_t sbe = e8m0_of(sbb);
+    uint32_t sbe = 0;
+    if constexpr (ROW128) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sbe |= e8m0_of(sc[BM + wn * CFG::WTN + 16 * j + l16]) << (8 * j);
+    } else {
+      sbe = e8m0_of(sbb);
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
       if (i < CR)
-        issue_copies<CFG, OPB_T>(t, plan, scoff, ra, rb, rs, (i * LOADS) / CR, ((i + 1) * LOADS) / CR, nops, nsc,
+        issue_copies<CFG, OPB_T, ROW128>(t, plan, scoff, ra, rb, rs, (i * LOADS) / CR, ((i + 1) * LOADS) / CR, nops, nsc,
                                  wave, blk);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_e8m0_sel(0, i % 4, bfr[j], afr, acc[i][j], sbe, sae[i / 4]);
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = mfma_e8m0_sel(ROW128 ? j : 0, i % 4, bfr[j], afr, acc[i][j], sbe, sae[i / 4]);
       afr = anext;
       __builtin_amdgcn_sched_barrier(0);
     }
     return;
   }
 
-  float scl[TM];  // fl32(sA * sB) per row tile
+  float scl[TM];  // fl32(sA * sB) per row tile (block scales)
 #pragma unroll
-  for (int i = 0; i < TM; ++i) scl[i] = sa[i] * sbb;
+  for (int i = 0; i < TM; ++i) scl[i] = ROW128 ? sa[i] : sa[i] * sbb;
   v4f ring[R];
   auto fold = [&](int kk) {
     const int i = kk / TN, j = kk % TN;
+    if constexpr (ROW128) {
+      // per-column scales: fl32(P * sB) then one FMA by sA, as the
+      // 128 x 128 tiles fold
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(ring[kk % R][r], scl[i], acc[i][j][r]);
+      for (int r = 0; r < 4; ++r) {
+        const float sb = r == 0 ? sbv[j].x : r == 1 ? sbv[j].y : r == 2 ? sbv[j].z : sbv[j].w;
+        acc[i][j][r] = __builtin_fmaf(ring[kk % R][r] * sb, scl[i], acc[i][j][r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(ring[kk % R][r], scl[i], acc[i][j][r]);
+    }
   };
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const v8i anext = i + 1 < TM ? load_a(i + 1) : afr;
     if (i < CR)
-      issue_copies<CFG, OPB_T>(t, plan, scoff, ra, rb, rs, (i * LOADS) / CR, ((i + 1) * LOADS) / CR, nops, nsc, wave,
+      issue_copies<CFG, OPB_T, ROW128>(t, plan, scoff, ra, rb, rs, (i * LOADS) / CR, ((i + 1) * LOADS) / CR, nops, nsc, wave,
                                blk);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -721,20 +752,20 @@ __device__ __forceinline__ void compute_group_rows(const uint8_t* ops, const flo
 // iteration, one per LDS stage, with no branch inside the iteration (a
 // branch there lets the compiler sink the MFMAs of the first group below it,
 // past the row fences); an odd last group runs after the loop.
-template <class CFG, bool OPB_T, bool P2>
+template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void gemm_loop_rows(const TileArgs& t, uint8_t* ops0, uint8_t* ops1, float* sc0, float* sc1,
                                                v4f (&acc)[CFG::TM][CFG::TN]) {
   const int g0 = t.g0, G = t.g1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int blk = wave < CFG::S_BLOCKS ? wave : 0;  // this wave's 64-float block of the scale buffer
-  CopyPlan<CFG, OPB_T, false> plan;
+  CopyPlan<CFG, OPB_T, ROW128> plan;
   plan.init(t);
   const uint32_t scoff = plan.sc_offset(t);
-  GroupCursor<CFG, OPB_T> cur;
+  GroupCursor<CFG, OPB_T, ROW128> cur;
   cur.init(t, g0, blk * 64 < CFG::BM);
   if (g0 < G)  // no groups (an expert without tokens): C = 0
-    issue_copies<CFG, OPB_T>(t, plan, scoff, cur.ra(true), cur.rb(true), cur.rs(true), 0,
-                             CopyPlan<CFG, OPB_T, false>::LOADS, ops0, sc0, wave, blk);
+    issue_copies<CFG, OPB_T, ROW128>(t, plan, scoff, cur.ra(true), cur.rb(true), cur.rs(true), 0,
+                             CopyPlan<CFG, OPB_T, ROW128>::LOADS, ops0, sc0, wave, blk);
   cur.advance();
   auto step = [&](int gnext, uint8_t* ops, float* sc, uint8_t* nops, float* nsc) {
     // This group has landed in `ops` once this lane's copies are complete;
@@ -745,7 +776,7 @@ __device__ __forceinline__ void gemm_loop_rows(const TileArgs& t, uint8_t* ops0,
     const bool on = gnext < G;
     const v4i ra = cur.ra(on), rb = cur.rb(on), rs = cur.rs(on);
     __builtin_amdgcn_sched_barrier(0);
-    compute_group_rows<CFG, OPB_T, P2>(ops, sc, acc, t, plan, scoff, ra, rb, rs, nops, nsc, wave, blk);
+    compute_group_rows<CFG, OPB_T, ROW128, P2>(ops, sc, acc, t, plan, scoff, ra, rb, rs, nops, nsc, wave, blk);
     __builtin_amdgcn_sched_barrier(0);
     cur.advance();
   };
@@ -774,7 +805,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if constexpr (row_pipelined<CFG, ROW128>()) {
-    gemm_loop_rows<CFG, OPB_T, P2>(t, ops0, ops1, sc0, sc1, acc);
+    gemm_loop_rows<CFG, OPB_T, ROW128, P2>(t, ops0, ops1, sc0, sc1, acc);
   } else {
     CopyPlan<CFG, OPB_T, ROW128> plan;
     plan.init(t);
@@ -1333,13 +1364,12 @@ static fp8blk_status_t gemm_dense(int64_t M, int64_t N, int64_t K, const uint8_t
   }
   // 256x256 tiles when they give at least half a wave of workgroups over
   // the 256 CUs, 128x128 tiles otherwise.
+  const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
   if (bscale_mode == FP8BLK_BSCALE_ROW128) {
-    const int64_t row_tiles = ceil_div(M, RowCfg::BM) * ceil_div(N, RowCfg::BN);
-    if (row_tiles >= 128)
-      return dispatch_dense<RowCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
+    if (big_tiles >= 128)
+      return dispatch_dense<BigCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
     return dispatch_dense<SmallCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   }
-  const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
   if (big_tiles >= 128)
     return dispatch_dense<BigCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   return dispatch_dense<SmallCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);

@@ -90,6 +90,30 @@ def test_exact_small_integers_bitwise(opB, mode):
     assert np.array_equal(C.astype(np.float64), R)
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("opB,mode", CASES)
+def test_exact_small_integers_bitwise_256x256_tiles(opB, mode, pow2):
+    """The same exact case on a shape whose 256 x 256 tiles fill the GPU (the
+    row-pipelined loop), fold and power-of-two paths, with ragged edges."""
+    rng = np.random.default_rng(13)
+    M, N, K = 4100, 2050, 384
+    G = K // 128
+    qA = _small_int_codes(rng, (M, K))
+    qB = _small_int_codes(rng, (K, N) if opB == oracle.OP_N else (N, K))
+    sA = np.exp2(rng.integers(-3, 4, size=(G, M))).astype(np.float32)
+    NB = -(-N // 128)
+    if mode == oracle.BSCALE_ROW128:
+        sB = np.exp2(rng.integers(-3, 4, size=(G, N))).astype(np.float32)
+    else:
+        sB = np.exp2(rng.integers(-3, 4, size=(G, NB) if opB == oracle.OP_N else (NB, G))).astype(np.float32)
+    print(f"[gemm] exact 256x256 tiles {M}x{N}x{K} opB={opB} mode={mode} pow2={pow2}", flush=True)
+    C = fb.gemm_fp8_blockscaled(u8_dev(qA), f32_dev(sA), u8_dev(qB), f32_dev(sB), opB=opB, bscale_mode=mode,
+                                pow2_scales=pow2)
+    torch.cuda.synchronize()
+    R = oracle.gemm_blockscaled(qA, sA, qB, sB, opB, mode)
+    assert np.array_equal(np_f32(C).astype(np.float64), R)
+
+
 def test_identity_b_bitwise():
     rng = np.random.default_rng(12)
     M, K = 200, 384
