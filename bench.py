@@ -14,7 +14,9 @@ included).  `roofline` reports the GEMM kernel alone (average duration from
 HIP events around each launch in the timed region) against the dense FP8
 MFMA peak.  `kernels` adds each kernel's time and roofline fraction (the
 quantizers from a second pass of the same steps with events between all
-kernels), and `extras` times the other workloads' kernels
+kernels; beside each quantizer, `stream_us` times a plain streaming kernel
+moving the same bytes over the same buffers and `frac_stream` = stream_us /
+us), and `extras` times the other workloads' kernels
 (backward Dgrad/Wgrad, the accumulation study, the MoE grouped GEMMs).
 `cpu_baseline` times the CPU oracle on the whole step, repeated for at least 10 s.
 
@@ -113,6 +115,11 @@ class HipEvents:
         self.pool = []
 
 
+def progress(msg):
+    """One progress line on stderr (the JSON result goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def warm_up(torch, fn, min_seconds):
     """Run fn(i) until at least min_seconds of GPU work have passed: the GPU
     raises its clocks only after tens of milliseconds under load."""
@@ -157,6 +164,18 @@ def timed_events(torch, fn, reps):
     ts = sorted(hev.ms(a, b) for a, b in pairs)
     hev.release()
     return ts[len(ts) // 2]
+
+
+def stream_ms(torch, fb, srcs, reps):
+    """Median duration (ms) of the streaming probe (16 bytes read, 8 written
+    per chunk, no tile logic) over the given BF16 inputs, each into a buffer of
+    half its size: the quantizers' traffic at the same size and rotation,
+    the practical ceiling their times are set against."""
+    dsts = [torch.empty(x.numel(), dtype=torch.uint8, device=x.device) for x in srcs]
+    n = len(srcs)
+    t = timed_events(torch, lambda i: fb.stream_probe(srcs[i % n], dsts[i % n]), reps)
+    del dsts
+    return t
 
 
 def main():
@@ -208,12 +227,14 @@ def main():
                 ev["q1x128"].append((e0, e1))
                 ev["qblock"].append((e1, e2))
 
+    progress("warm-up")
     for i in range(args.warmup):
         step(i)
     warm_up(torch, step, args.warmup_seconds)
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps, synchronized on both sides.
+    progress(f"timed: {args.steps} steps")
     t0 = time.perf_counter()
     start = hev.record()
     for i in range(args.steps):
@@ -241,20 +262,23 @@ def main():
         step(i, record=True, per_kernel=True)
     torch.cuda.synchronize()
     t_q1, t_qb = avg("q1x128"), avg("qblock")
+    st_a = stream_ms(torch, fb, A, 40)
+    st_w = stream_ms(torch, fb, W, 40)
     gemm_tflops = flops / (t_g * 1e-3) / 1e12
     q1_gbs = M * K * QUANT_BYTES_1X128 / (t_q1 * 1e-3) / 1e9
     qb_gbs = K * N * QUANT_BYTES_BLOCK / (t_qb * 1e-3) / 1e9
     kernels = {
         "quantize_1x128": {"us": round(t_q1 * 1e3, 2), "GB/s": round(q1_gbs, 1), "frac_hbm": round(q1_gbs / HBM_PEAK_GBS, 4),
-                           **pct("q1x128")},
+                           **pct("q1x128"), "stream_us": round(st_a * 1e3, 2), "frac_stream": round(st_a / t_q1, 3)},
         "quantize_block128": {"us": round(t_qb * 1e3, 2), "GB/s": round(qb_gbs, 1), "frac_hbm": round(qb_gbs / HBM_PEAK_GBS, 4),
-                              **pct("qblock")},
+                              **pct("qblock"), "stream_us": round(st_w * 1e3, 2), "frac_stream": round(st_w / t_qb, 3)},
         "gemm_fp8_blockscaled": {"us": round(t_g * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
                                  "frac_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), **p_g},
     }
 
     extras = {}
     if not args.no_extras:
+        progress("extras: power-of-two step, BF16 and fused epilogues")
         # The same step with power-of-two scales (the pages' variant for some
         # activations): both quantizers in pow2 mode and the GEMM applying
         # the scales inside the matrix cores.
@@ -318,6 +342,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
+        progress("cpu baseline")
         cpu = cpu_baseline(np, synthetic, A0, W0, M, N, K)
 
     out = {
@@ -354,9 +379,17 @@ def n_sets(nbytes, total=640e6):
     return max(2, int(-(-total // nbytes)))
 
 
+class _Results(dict):
+    """Extras' results; each new entry is announced on stderr."""
+
+    def __setitem__(self, k, v):
+        progress(f"extras: {k}")
+        super().__setitem__(k, v)
+
+
 def run_extras(torch, fb, synthetic, dev, np):
     """Per-kernel timings on the other workloads (HIP events, few reps)."""
-    res = {}
+    res = _Results()
     reps = 10
     # launch floor: the smallest launches of the library (one quantizer
     # workgroup, one 128x128x128 GEMM tile), beside which the small workloads'
@@ -425,8 +458,9 @@ def run_extras(torch, fb, synthetic, dev, np):
                          if fn is not fb.quantize_128x1 else
                          fn(sets[i % ns][0], qT=sets[i % ns][1], s=sets[i % ns][2]), max(reps, 2 * ns))
         gbs = x.numel() * bpe / (t * 1e-3) / 1e9
+        ts = stream_ms(torch, fb, [st[0] for st in sets], max(reps, 2 * ns))
         res[name] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                     "sets": ns}
+                     "sets": ns, "stream_us": round(ts * 1e3, 2), "frac_stream": round(ts / t, 3)}
         del sets
     # the pages' backward path: the cached 1x128 FP8 copy re-quantized to
     # 128x1, for dY and for the activations X (the cached forward input)
@@ -587,7 +621,7 @@ def run_extras(torch, fb, synthetic, dev, np):
         "frac_mfma": round(fl / t / 1e9 / FP8_PEAK_TFLOPS, 4), "frac_hbm": round(byts / t / 1e6 / HBM_PEAK_GBS, 4)}
     del Wb, AT, BT, sAT, sBT, dO, H
     torch.cuda.empty_cache()
-    return res
+    return dict(res)
 
 
 def cpu_baseline(np, synthetic, A0, W0, M, N, K):

@@ -52,6 +52,7 @@ _SIGNATURES = {
                                                     _vp, _u32, _vp, _i64, _i64, _vp]),
     "fp8blk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "fp8blk_mfma_probe": (_int, [_int, _vp, _vp, _vp, _vp]),
+    "fp8blk_stream_probe": (_int, [_vp, _i64, _vp, _vp]),
     "fp8blk_gemm_fp8_blockscaled_noalloc": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _vp, _int,
                                                    _vp, _i64, _vp]),
     "fp8blk_status_string": (ctypes.c_char_p, [_int]),
@@ -104,6 +105,17 @@ def mfma_probe(A: torch.Tensor, B: torch.Tensor, instr: int = 0) -> torch.Tensor
     C = torch.empty(16, 16, dtype=torch.float32, device=A.device)
     _check(lib().fp8blk_mfma_probe(instr, _ptr(A), _ptr(B), _ptr(C), _stream()), "mfma_probe")
     return C
+
+
+def stream_probe(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Plain streaming kernel with the quantizers' traffic (see
+    fp8blk_stream_probe): reads src (a multiple of 16 bytes), writes half as
+    many bytes into dst; both contiguous on the device."""
+    nb = src.numel() * src.element_size()
+    assert src.is_contiguous() and dst.is_contiguous() and nb % 16 == 0
+    assert dst.numel() * dst.element_size() >= nb // 2
+    _check(lib().fp8blk_stream_probe(_ptr(src), nb // 16, _ptr(dst), _stream()), "stream_probe")
+    return dst
 
 
 def _check(code: int, what: str):

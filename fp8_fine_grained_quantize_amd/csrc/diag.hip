@@ -1,9 +1,16 @@
-// Diagnostic entry point: one 16x16 tile product over 128 FP8 (E4M3) k by a
+// Diagnostic entry points.
+//
+// fp8blk_mfma_probe: one 16x16 tile product over 128 FP8 (E4M3) k by a
 // chosen matrix-core instruction, returned raw.  The GEMMs' error model rests
 // on how the matrix cores add the products inside one instruction (the pages
 // describe the H800's limited tensor-core accumulation and promote partial
 // sums into FP32 at a fixed K interval for that reason [p2¶3, p5¶4]); this
 // call lets a test pin that behaviour on the device.
+//
+// fp8blk_stream_probe: a plain streaming kernel with the quantizers' traffic
+// (16 bytes read, 8 written per 16-byte chunk) and no arithmetic to speak of,
+// which gives the HBM rate that a kernel of this shape reaches on the device
+// at a given size, the practical ceiling the quantizers are compared with.
 // Citations [pN¶k]: N-th page of the source collection, k-th paragraph
 // (p2 = inprokorea.com wr_id 735329, p5 = inprokorea.com wr_id 890463).
 #include "host_common.h"
@@ -45,6 +52,30 @@ __global__ __launch_bounds__(64) void k_mfma_probe(int instr, const uint8_t* __r
   for (int r = 0; r < 4; ++r) C[(4 * kq + r) * 16 + row] = d[r];
 }
 
+// Grid-stride over 16-byte chunks, two chunks in flight per lane; each chunk's
+// words are folded pairwise (x ^ y, z ^ w) into the 8 bytes written, so every
+// byte read is used.  Two chunks per lane and four workgroups of 256 lanes
+// per compute unit measured the best of 1-8 chunks and 4-32 workgroups per
+// compute unit (88 MB and 25 MB moved, rotating buffers).
+__global__ __launch_bounds__(256) void k_stream_probe(const uint4* __restrict__ src, uint2* __restrict__ dst,
+                                                      int64_t n) {
+  constexpr int U = 2;
+  const int64_t stride = (int64_t)gridDim.x * 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n; base += stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      v[u] = i < n ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      if (i < n) dst[i] = make_uint2(v[u].x ^ v[u].y, v[u].z ^ v[u].w);
+    }
+  }
+}
+
 }  // namespace fp8blk
 
 using namespace fp8blk;
@@ -54,5 +85,17 @@ extern "C" fp8blk_status_t fp8blk_mfma_probe(int instr, const uint8_t* A, const 
   if (A == nullptr || B == nullptr || C == nullptr || !aligned(A, 16) || !aligned(B, 16) || !aligned(C, 4))
     return FP8BLK_ERR_INVALID_ARG;
   hipLaunchKernelGGL(k_mfma_probe, dim3(1), dim3(64), 0, as_stream(stream), instr, A, B, C);
+  return launch_status();
+}
+
+extern "C" fp8blk_status_t fp8blk_stream_probe(const void* src, int64_t chunks, void* dst, void* stream) {
+  if (chunks < 0) return FP8BLK_ERR_INVALID_ARG;
+  if (chunks == 0) return FP8BLK_OK;
+  if (src == nullptr || dst == nullptr || !aligned(src, 16) || !aligned(dst, 8)) return FP8BLK_ERR_INVALID_ARG;
+  int64_t grid = ceil_div(chunks, (int64_t)512);
+  const int64_t cap = (int64_t)device_cus() * 4;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(k_stream_probe, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
+                     reinterpret_cast<const uint4*>(src), reinterpret_cast<uint2*>(dst), chunks);
   return launch_status();
 }

@@ -90,100 +90,38 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// 128x128 blocks, persistent and software-pipelined: a workgroup of NT lanes
-// takes blocks b, b + grid, ...; lane (sub = tid/16, c16 = tid%16) holds
-// chunk c16 of rows sub, sub + NT/16, ... (2048/NT chunks).  The next block's
-// loads are issued before the current block's maximum is reduced and its
-// codes are written.  The cross-wave maximum goes through one of two LDS
-// slots, alternating per block, so one barrier per block suffices.
+// 128x128 blocks, one block per workgroup of NT lanes: lane (sub = tid/16,
+// c16 = tid%16) holds chunk c16 of rows sub, sub + NT/16, ... (2048/NT
+// chunks of 8 values).  The cross-wave maximum goes through LDS.  Interior
+// blocks load and store through one base pointer each.  At NT = 512 the
+// kernel needs 52 VGPRs, so every workgroup of a 1792-block weight is
+// resident from the start; measured against a persistent kernel that
+// prefetched its next block (118 VGPRs, 4 workgroups per compute unit) with
+// rotating sets on one box: 7168x4096 22.5 -> 20.6 us, 7168x2048 15.7 ->
+// 13.1 us, within 3 % of a plain kernel that streams the same bytes (16 read,
+// 8 written per lane step); 256 and 1024 lanes were slower.  It also replaced
+// a kernel with one wave per block and the whole block in registers: 4 %
+// faster at 8064 blocks, 1 % slower at 16384.
 // ---------------------------------------------------------------------------
 template <bool POW2, int NT>
 __global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restrict__ w, int64_t R, int64_t C,
                                                         int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ s, int64_t GR, int64_t GC) {
+                                                        float* __restrict__ s, int64_t GC) {
   constexpr int CH = 2048 / NT, RSTEP = NT / 16, NWAVE = NT / 64;
-  __shared__ uint32_t red[2][NWAVE];
-  const int sub = threadIdx.x >> 4;
-  const int c16 = threadIdx.x & 15;
-  const int64_t grid = gridDim.x;
-  const int64_t dbi = grid / GC, dbj = grid % GC;
-  int64_t bi = (int64_t)blockIdx.x / GC, bj = (int64_t)blockIdx.x % GC;
-  auto load = [&](int64_t i, int64_t j, uint4 (&v)[CH]) {
-    const int64_t col = j * 128 + c16 * 8;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t row = i * 128 + sub + RSTEP * c;
-      v[c] = make_uint4(0u, 0u, 0u, 0u);
-      if (i < GR && row < R && col < C) v[c] = load_chunk8(w + row * ldw + col, C - col);
-    }
-  };
-  uint4 cur[CH], nxt[CH];
-  load(bi, bj, cur);
-  int par = 0;
-  while (bi < GR) {
-    int64_t ni = bi + dbi, nj = bj + dbj;
-    if (nj >= GC) {
-      nj -= GC;
-      ni += 1;
-    }
-    load(ni, nj, nxt);
-    uint32_t a = 0;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) a = max(a, chunk_abs_max(cur[c]));
-    a = row16_max(a);
-    a = max(a, (uint32_t)__shfl_xor((int)a, 16));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 32));
-    if ((threadIdx.x & 63) == 0) red[par][threadIdx.x >> 6] = a;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NWAVE; ++k) a = max(a, red[par][k]);
-    const TileScale ts = make_scale<POW2, true>(a << 16);
-    const int64_t col = bj * 128 + c16 * 8;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t row = bi * 128 + sub + RSTEP * c;
-      const uint2 codes = quantize8<POW2>(cur[c], ts);
-      if (row < R && col < C) store_chunk8(q + row * ldq + col, C - col, codes);
-    }
-    if (threadIdx.x == 0) s[bi * GC + bj] = ts.s;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) cur[c] = nxt[c];
-    bi = ni;
-    bj = nj;
-    par ^= 1;
-  }
-}
-
-
-// Large weights: one wave per 128x128 block (four blocks per workgroup), the
-// whole block in the lane's registers (32 chunks of 8 values), so the block
-// maximum needs no LDS and no barrier.  Interior blocks load and store
-// through one base pointer each (the bounds-checked form keeps a 64-bit
-// address per chunk live and needs 276 VGPRs instead of 159).  Measured
-// against the persistent kernel (rotating sets, one box, bitwise-identical
-// results): 4096 blocks 14 % slower, 8064 blocks 5 % faster, 16384 blocks
-// 10 % faster; the launcher switches above 6144 blocks.
-template <bool POW2>
-__global__ __launch_bounds__(256) void k_quant_block128_w(const uint16_t* __restrict__ w, int64_t R, int64_t C,
-                                                           int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
-                                                           float* __restrict__ s, int64_t GR, int64_t GC) {
-  constexpr int CH = 32;
-  const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= GR * GC) return;
-  const int64_t bi = blk / GC, bj = blk % GC;
-  const int sub = lane >> 4, c16 = lane & 15;
+  __shared__ uint32_t red[NWAVE];
+  const int sub = threadIdx.x >> 4, c16 = threadIdx.x & 15;
+  const int64_t bi = (int64_t)blockIdx.x / GC, bj = (int64_t)blockIdx.x % GC;
   const int64_t col = bj * 128 + c16 * 8;
-  uint4 v[CH];
   const bool interior = (bi + 1) * 128 <= R && (bj + 1) * 128 <= C;
+  uint4 v[CH];
   if (interior) {
     const uint16_t* p = w + (bi * 128 + sub) * ldw + col;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) v[c] = *reinterpret_cast<const uint4*>(p + (int64_t)(4 * c) * ldw);
+    for (int c = 0; c < CH; ++c) v[c] = *reinterpret_cast<const uint4*>(p + (int64_t)(RSTEP * c) * ldw);
   } else {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int64_t row = bi * 128 + sub + 4 * c;
+      const int64_t row = bi * 128 + sub + RSTEP * c;
       v[c] = make_uint4(0u, 0u, 0u, 0u);
       if (row < R && col < C) v[c] = load_chunk8(w + row * ldw + col, C - col);
     }
@@ -194,20 +132,24 @@ __global__ __launch_bounds__(256) void k_quant_block128_w(const uint16_t* __rest
   a = row16_max(a);
   a = max(a, (uint32_t)__shfl_xor((int)a, 16));
   a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NWAVE; ++k) a = max(a, red[k]);
   const TileScale ts = make_scale<POW2, true>(a << 16);
   if (interior) {
     uint8_t* o = q + (bi * 128 + sub) * ldq + col;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) *reinterpret_cast<uint2*>(o + (int64_t)(4 * c) * ldq) = quantize8<POW2>(v[c], ts);
+    for (int c = 0; c < CH; ++c) *reinterpret_cast<uint2*>(o + (int64_t)(RSTEP * c) * ldq) = quantize8<POW2>(v[c], ts);
   } else {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int64_t row = bi * 128 + sub + 4 * c;
+      const int64_t row = bi * 128 + sub + RSTEP * c;
       const uint2 codes = quantize8<POW2>(v[c], ts);
       if (row < R && col < C) store_chunk8(q + row * ldq + col, C - col, codes);
     }
   }
-  if (lane == 0) s[bi * GC + bj] = ts.s;
+  if (threadIdx.x == 0) s[bi * GC + bj] = ts.s;
 }
 
 
@@ -237,8 +179,6 @@ __global__ __launch_bounds__(256) void k_quant_block128_w(const uint16_t* __rest
 // workgroups cost 7 % on dOut [65536][7168].
 // ---------------------------------------------------------------------------
 constexpr int Q128X1_CW = 64;
-// Blocks above which quantize_block128 takes one wave per block.
-constexpr int64_t FP8BLK_BLOCK128_WAVE_MIN = 6144;
 
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   const uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
@@ -472,12 +412,21 @@ __global__ __launch_bounds__(256) void k_quant_128x1_c64(const uint16_t* __restr
 // Re-quantization of a cached 1x128-quantized activation into transposed
 // 128x1 tiles [p5¶4]: codes are decoded by the hardware (exact), multiplied by
 // their 1x128 scale in FP32 (one rounding), and the resulting FP32 values are
-// quantized along tokens exactly as k_quant_128x1 quantizes BF16 values.  The
-// dequantized values are general FP32 numbers, outside the domain the
-// division shortcut was checked on, so the default mode divides per element
-// (IEEE); power-of-two scales multiply by the exact reciprocal.
+// quantized along tokens exactly as k_quant_128x1 quantizes BF16 values.
 // One workgroup per 128 tokens x 128 channels; the 128-channel block is also
 // exactly one 1x128 scale group, so each token has one input scale here.
+//
+// The dequantized values are general FP32 numbers, outside the domain the
+// BF16 division shortcut was checked on.  Default mode: the quotient is
+// fl32(x * r), r = fl64(1 / s) formed once per column in FP64 and the product
+// taken in FP64.  That equals IEEE fl32(x / s) for all FP32 x and s: with x
+// and s of 24-bit significands, a quotient that is not itself a rounding
+// midpoint of FP32 (in binary it never is) lies at least 2^-49 (relative)
+// away from every midpoint, while the FP64 product is within 2^-52 of x / s,
+// so both round to the same FP32 value.  This replaced an IEEE FP32 division
+// per element that made the kernel ALU-bound.  Values past +-448 are
+// possible only for a subnormal scale; a tile with one gets the clamp.
+// Power-of-two scales multiply by the exact FP32 reciprocal.
 // ---------------------------------------------------------------------------
 typedef float v2f __attribute__((ext_vector_type(2)));
 
@@ -494,6 +443,7 @@ __global__ __launch_bounds__(256) void k_requant_128x1(const uint8_t* __restrict
                                                         int64_t ldqT, float* __restrict__ sT) {
   __shared__ uint32_t red[4][16][8];
   __shared__ float sh_s[128], sh_r[128];
+  __shared__ double sh_r64[128];
   __shared__ int sh_slow[128];
   __shared__ __align__(16) uint8_t tile[128 * 128];
 
@@ -539,6 +489,7 @@ __global__ __launch_bounds__(256) void k_requant_128x1(const uint8_t* __restrict
     for (int i = 0; i < 8; ++i) red[tid >> 6][c16][i] = m[i];
   }
   __syncthreads();
+  bool slow_col = false;
   if (tid < 128) {
     const int c = tid;
     uint32_t a = 0;
@@ -547,23 +498,35 @@ __global__ __launch_bounds__(256) void k_requant_128x1(const uint8_t* __restrict
     const TileScale ts = make_scale<POW2, false>(a);
     sh_s[c] = ts.s;
     sh_r[c] = ts.r;
+    if (!POW2) sh_r64[c] = 1.0 / (double)ts.s;
     sh_slow[c] = ts.slow ? 1 : 0;
     if (c0 + c < C) sT[(int64_t)blockIdx.y * C + c0 + c] = ts.s;
+    slow_col = POW2 ? ts.slow : ts.s < 0x1p-126f;
   }
-  __syncthreads();
+  const bool any_slow = __syncthreads_or(slow_col ? 1 : 0) != 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = c16 * 8 + i;
-    TileScale ts;
-    ts.s = sh_s[c];
-    ts.r = sh_r[c];
-    ts.slow = sh_slow[c] != 0;
     float y[8];
+    if (POW2) {
+      TileScale ts;
+      ts.s = sh_s[c];
+      ts.r = sh_r[c];
+      ts.slow = sh_slow[c] != 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = quotient_fast<POW2, false>(xv[j][i], ts);
-    if (POW2 && __builtin_expect(ts.slow, 0)) {
+      for (int j = 0; j < 8; ++j) y[j] = quotient_fast<true, false>(xv[j][i], ts);
+      if (__builtin_expect(ts.slow, 0)) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) y[j] = quotient_slow(xv[j][i], ts.s);
+        for (int j = 0; j < 8; ++j) y[j] = quotient_slow(xv[j][i], ts.s);
+      }
+    } else {
+      const double r64 = sh_r64[c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = (float)((double)xv[j][i] * r64);
+      if (__builtin_expect(any_slow, 0)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = fminf(fmaxf(y[j], -kE4M3Max), kE4M3Max);
+      }
     }
     uint2 codes;
     codes.x = pack4_e4m3(y[0], y[1], y[2], y[3]);
@@ -621,31 +584,15 @@ extern "C" fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R
   const int64_t GR = ceil_div(R, 128), GC = ceil_div(C, 128);
   if (!vec_ok(s, GR * GC)) return FP8BLK_ERR_INVALID_ARG;
   if (R == 0 || C == 0) return FP8BLK_OK;
-  if (GR * GC > FP8BLK_BLOCK128_WAVE_MIN) {
-    const int64_t wgs = ceil_div(GR * GC, (int64_t)4);
-    if (wgs > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
-    if (flags & FP8BLK_SCALE_POW2)
-      hipLaunchKernelGGL(k_quant_block128_w<true>, dim3((unsigned)wgs), dim3(256), 0, as_stream(stream), w, R, C, ldw,
-                         q, ldq, s, GR, GC);
-    else
-      hipLaunchKernelGGL(k_quant_block128_w<false>, dim3((unsigned)wgs), dim3(256), 0, as_stream(stream), w, R, C, ldw,
-                         q, ldq, s, GR, GC);
-    return launch_status();
-  }
-  // Persistent grid of up to 8 workgroups of 256 lanes per compute unit, each
-  // taking every grid-th block.  At the kernel's register count 4 of them are
-  // resident per compute unit at a time and the rest start as those finish;
-  // smaller grids that keep every workgroup resident measured slower.
-  constexpr int NT = 256;
-  int64_t grid = GR * GC;
-  const int64_t cap = (int64_t)device_cus() * 8;
-  if (grid > cap) grid = cap;
+  constexpr int NT = 512;
+  const int64_t blocks = GR * GC;
+  if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
   if (flags & FP8BLK_SCALE_POW2)
-    hipLaunchKernelGGL((k_quant_block128<true, NT>), dim3((unsigned)grid), dim3(NT), 0, as_stream(stream), w, R, C, ldw,
-                       q, ldq, s, GR, GC);
+    hipLaunchKernelGGL((k_quant_block128<true, NT>), dim3((unsigned)blocks), dim3(NT), 0, as_stream(stream), w, R, C,
+                       ldw, q, ldq, s, GC);
   else
-    hipLaunchKernelGGL((k_quant_block128<false, NT>), dim3((unsigned)grid), dim3(NT), 0, as_stream(stream), w, R, C,
-                       ldw, q, ldq, s, GR, GC);
+    hipLaunchKernelGGL((k_quant_block128<false, NT>), dim3((unsigned)blocks), dim3(NT), 0, as_stream(stream), w, R, C,
+                       ldw, q, ldq, s, GC);
   return launch_status();
 }
 

@@ -329,6 +329,19 @@ fp8blk_status_t fp8blk_grouped_wgrad_fp8_blockscaled(int64_t G, const int32_t* g
  */
 fp8blk_status_t fp8blk_mfma_probe(int instr, const uint8_t* A, const uint8_t* B, float* C, void* stream);
 
+/*
+ * Diagnostic: a plain streaming kernel with the quantizers' HBM traffic
+ * pattern (BF16 in, one byte per element out: 16 bytes read and 8 bytes
+ * written per 16-byte chunk), so that a quantizer's time can be set against
+ * what a kernel of the same traffic and no tile logic takes on the device.
+ *   src     DEVICE, `chunks` 16-byte chunks, 16-byte aligned (read only).
+ *   chunks  number of 16-byte chunks, >= 0 (0: nothing is read or written).
+ *   dst     DEVICE, 8 * chunks bytes, 8-byte aligned; byte pairs of words
+ *           (x ^ y, z ^ w) of each chunk (x, y, z, w its 4-byte words).
+ *   FP8BLK_ERR_INVALID_ARG for chunks < 0, a null or misaligned pointer.
+ */
+fp8blk_status_t fp8blk_stream_probe(const void* src, int64_t chunks, void* dst, void* stream);
+
 /* Workspace that lets fp8blk_gemm_fp8_blockscaled split K for this shape
  * (G = 1), for the current device; 0 when it would not split.  The grouped
  * GEMM (G > 1) needs none. */
@@ -337,8 +350,9 @@ size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
 /* Human-readable name of a status code (static string). */
 const char* fp8blk_status_string(fp8blk_status_t status);
 
-/* ABI version of this header: 4 (2 added the MoE backward entry points, 3 the
- * BF16 output flag and the quantize-on-store GEMM, 4 the matrix-core probe). */
+/* ABI version of this header: 5 (2 added the MoE backward entry points, 3 the
+ * BF16 output flag and the quantize-on-store GEMM, 4 the matrix-core probe
+ * and the allocation-free GEMM, 5 the streaming probe). */
 int fp8blk_abi_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fb.abi_version() == 4
+    assert fb.abi_version() == 5
     assert fb.token_group_slots(65536, 256) == 512 + 256
     assert fb.token_group_slots(100, 3) == 3 and fb.token_group_slots(-1, 3) == 0
     assert fb.status_string(0) == "FP8BLK_OK"
@@ -92,6 +92,20 @@ def test_requantize_validation():
     assert f(FAKE, FAKE, 256, 128, 128, FAKE, 256, FAKE, 4, NULL) == INVALID
     assert f(FAKE, FAKE, 256, 128, 100, FAKE, 256, FAKE, 0, NULL) == INVALID
     assert f(NULL, NULL, 0, 128, 128, NULL, 16, NULL, 0, NULL) == OK
+
+
+def test_probe_validation():
+    """Diagnostic entry points reject bad arguments before any launch."""
+    f = fb.lib().fp8blk_mfma_probe
+    assert f(2, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert f(0, NULL, FAKE, FAKE, NULL) == INVALID
+    assert f(0, MIS, FAKE, FAKE, NULL) == INVALID
+    g = fb.lib().fp8blk_stream_probe
+    assert g(FAKE, -1, FAKE, NULL) == INVALID
+    assert g(NULL, 4, FAKE, NULL) == INVALID
+    assert g(MIS, 4, FAKE, NULL) == INVALID
+    assert g(FAKE, 4, P(0x100004), NULL) == INVALID
+    assert g(NULL, 0, NULL, NULL) == OK
 
 
 def _gemm(M=256, N=256, K=256, A=FAKE, lda=256, sA=FAKE, B=FAKE, ldb=256, opB=0, sB=FAKE, mode=0, C=FAKE,

@@ -81,14 +81,14 @@ def test_block128_past_2g_elements():
 
 
 @pytest.mark.parametrize("pow2", [False, True])
-def test_block128_one_wave_per_block(pow2):
-    """Above 6144 blocks quantize_block128 takes one wave per block; ragged
+def test_block128_large_ragged_pitched(pow2):
+    """quantize_block128 on 6241 blocks: ragged
     row and column edges (10013 columns: the last block's rows end 1-7
     elements into a 16-byte chunk), a pitched view, outlier columns, both
     scale modes; every code and scale against the oracle."""
     R, C = 10000, 10013
-    assert (-(-R // 128)) * (-(-C // 128)) > 6144 and C % 8 != 0
-    print(f"[max] quantize_block128 one wave per block [{R}][{C}] pow2={pow2}", flush=True)
+    assert (-(-R // 128)) * (-(-C // 128)) == 6241 and C % 8 != 0
+    print(f"[max] quantize_block128 large ragged pitched [{R}][{C}] pow2={pow2}", flush=True)
     g = torch.Generator().manual_seed(31)
     x_cpu = synthetic.randn_bf16((R, C), 1.0, g, outlier_cols=3, outlier_factor=60.0)
     x = fb.as_pitched(x_cpu.cuda())
@@ -103,8 +103,7 @@ def test_block128_one_wave_per_block(pow2):
 
 def test_block128_stacked_expert_weights():
     """The 256 down-projection weights of the MoE workload quantized in one
-    launch on their stacked [256*2048][7168] tensor (57344 blocks, the
-    one-wave kernel) equal each expert's own quantization: 2048 is a multiple
+    launch on their stacked [256*2048][7168] tensor (57344 blocks) equal each expert's own quantization: 2048 is a multiple
     of 128, so the block grids coincide and the stacked scales are the
     per-expert tables back to back.  Checked against the oracle on four
     experts (first, last, two others)."""

@@ -135,6 +135,29 @@ def test_requantize_from_1x128():
         assert np.array_equal(np_f32(sT).view(np.uint32), sTo.view(np.uint32))
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_requantize_wide_range_and_subnormal_scales(pow2):
+    """Token rows scaled by 10^u, u uniform in [-30, 30], so that one 128-token
+    column tile mixes dequantized values of every magnitude (general FP32
+    quotients), and a 128 x 128 corner near the bottom of the BF16 range, so
+    that its 1x128 scales and its 128x1 scales are subnormal (the clamped
+    quotient).  Codes and scales bit for bit against the oracle."""
+    T, C = 640, 384
+    g = torch.Generator().manual_seed(41 + pow2)
+    mag = torch.pow(10.0, torch.rand(T, 1, generator=g) * 60 - 30)
+    x = (torch.randn(T, C, generator=g) * mag).to(torch.bfloat16)
+    x[:128, :128] = (torch.randn(128, 128, generator=g) * 1e-38).to(torch.bfloat16)
+    qo, so = oracle.quantize_1x128(bf16_bits(x))
+    assert np.any(so[0, :128] < np.float32(2.0 ** -126))
+    print(f"[requant] wide range pow2={pow2}", flush=True)
+    qT, sT = fb.requantize_128x1_from_1x128(u8_dev(qo), torch.from_numpy(so).cuda(), pow2=pow2)
+    torch.cuda.synchronize()
+    qTo, sTo = oracle.requantize_128x1_from_1x128(qo, so, pow2)
+    assert np.all(sTo[0, :128] < np.float32(2.0 ** -126))
+    assert np.array_equal(np_u8(qT), qTo)
+    assert np.array_equal(np_f32(sT).view(np.uint32), sTo.view(np.uint32))
+
+
 def test_empty_inputs_are_noops():
     x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
     q, s = fb.quantize_1x128(x)
