@@ -40,12 +40,16 @@ QUANT_BYTES_BLOCK = 2 + 1 + 4 / (128 * 128)
 
 # HBM traffic of one Fprop GEMM launch (4096 x 4096 x 7168, 256 x 256 tiles),
 # from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes over
-# `bench.py --steps 3 --warmup 1 --no-extras --no-cpu`, each scaled by what the
-# same counter reads for a plain 1 GiB device copy (FETCH_SIZE x2.0,
-# WRITE_SIZE x1.0).  Valid only for the GEMM source it was measured on
-# (sha256 below); reported as null otherwise.
-GEMM_TRAFFIC = {"sha256": "d9b07aec65f282c2986e73e8f78065359b3f6d1f4836b846d8e7ca9bdd610ae5",
-                "fetch_bytes": 178250454, "write_bytes": 67108864}
+# `bench.py --steps 3 --warmup 1 --warmup-seconds 0 --no-cpu` (64 dispatches
+# of this kernel), each scaled by what the same counter reads for a plain
+# 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  FETCH_SIZE counts
+# what the L2s request beyond themselves: 178 MB is the compulsory minimum of
+# the tile order, each of the 8 XCDs (one L2 each) reading the A and B panels
+# of its 4 x 8 block of tiles once (8 x 12 x 1.84 MB); sharing across XCDs is
+# left to the Infinity Cache.  Valid only for the GEMM source it was measured
+# on (sha256 below); reported as null otherwise.
+GEMM_TRAFFIC = {"sha256": "5776851b85ca02dcfa31b4a281f85a134dba12206af90d0346cdae305bce847d",
+                "fetch_bytes": 178240726, "write_bytes": 67108864}
 
 
 def parse():
