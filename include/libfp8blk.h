@@ -120,6 +120,8 @@ fp8blk_status_t fp8blk_quantize_1x128(const uint16_t* x, int64_t M, int64_t K, i
  *   s   [ceil(T/128)][C] FP32, dense: s[g*C + c] scales channel c over tokens
  *       [128g, 128g+128).  qT/s equal quantize_1x128 applied to x transposed.
  *   flags: 0 or FP8BLK_SCALE_POW2.
+ *   FP8BLK_ERR_UNSUPPORTED if ceil(T/128) > 65535 (T above 8 388 480 tokens:
+ *   the token groups are one launch dimension).
  */
 fp8blk_status_t fp8blk_quantize_128x1(const uint16_t* x, int64_t T, int64_t C, int64_t ldx,
                                       uint8_t* qT, int64_t ldqT, float* s, uint32_t flags,
@@ -146,6 +148,8 @@ fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R, int64_t C
  *   The dequantized value is fl32(dec(q) * s); it is then quantized exactly
  *   as fp8blk_quantize_128x1 quantizes a value.
  *   qT  [C][T] E4M3 codes (pitch ldqT >= T), sT [ceil(T/128)][C] FP32.
+ *   flags: 0 or FP8BLK_SCALE_POW2.
+ *   FP8BLK_ERR_UNSUPPORTED if ceil(T/128) > 65535, as for quantize_128x1.
  */
 fp8blk_status_t fp8blk_requantize_128x1_from_1x128(const uint8_t* q, const float* sq, int64_t T,
                                                    int64_t C, int64_t ldq, uint8_t* qT,
