@@ -815,7 +815,7 @@ __device__ __forceinline__ void gemm_loop_rows(const TileArgs& t, uint8_t* ops0,
 // LDS arrays (the two pipeline stages); the loop is unrolled by two so that
 // every access names its array at compile time, which lets the compiler see
 // that reading one stage does not have to wait for copies into the other.
-template <class CFG, bool OPB_T, bool ROW128, bool P2, int OM, bool SKIP = false>
+template <class CFG, bool OPB_T, bool ROW128, bool P2, int OM, bool SKIP = false, bool ONE_STAGE = false>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint8_t* ops1, float* sc0, float* sc1) {
   constexpr int TM = CFG::TM, TN = CFG::TN;
   const int g0 = t.g0, G = t.g1;
@@ -837,6 +837,21 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* ops0, uint
     // still issues its copies and meets every barrier.
     const int wrow0 = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / CFG::WAVES_N) * CFG::WTM;
     const bool computes = wrow0 < t.rows;
+    if constexpr (ONE_STAGE) {
+      // One LDS stage (ops1/sc1 unused): each group's copies are issued once
+      // every wave has finished reading the previous group.
+      for (int g = g0; g < G; ++g) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        if (computes) compute_group<CFG, OPB_T, ROW128, P2>(ops0, sc0, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 < G) {
+          __syncthreads();
+          plan.issue(t, g + 1, ops0, sc0);
+        }
+      }
+    } else
     for (int g = g0; g < G; g += 2) {
       // Group g has landed in stage 0 once this lane's copies are complete;
       // after the barrier every wave's copies are visible and every wave is
@@ -1189,6 +1204,16 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
 // Every expert's output has the same M x N tiles; tiles are enumerated expert
 // by expert, column tile by column tile, row tiles innermost.  An expert
 // without tokens gets dW_e = 0.
+// One LDS stage: an expert's tiles have only 2-3 K groups on average, so the
+// second stage bought little overlap and held the kernel to two workgroups
+// per compute unit by LDS; with one stage (35 KB) three are resident (by
+// registers) and one workgroup's stores overlap another's loads.  Measured
+// (interleaved, one box, bitwise identical) on the MoE down projection's
+// Wgrad: FP32 output 4.95 -> 4.63 ms, BF16 3.74 -> 3.41 ms.  Holding the
+// kernel to 128 VGPRs for four workgroups per compute unit spills.
+#ifndef FP8BLK_WGRAD_STAGES
+#define FP8BLK_WGRAD_STAGES 1
+#endif
 template <class CFG, bool P2, int OM>
 __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __restrict__ offsets, int64_t M, int64_t N,
                                                             const uint8_t* __restrict__ A, int64_t lda,
@@ -1197,7 +1222,14 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __rest
                                                             const float* __restrict__ sB, void* __restrict__ C,
                                                             int64_t ldc, int64_t strideC, int64_t tiles_m,
                                                             int64_t tiles_n) {
+#if FP8BLK_WGRAD_STAGES == 1
+  __shared__ __align__(16) uint8_t s_ops0[CFG::BUF_BYTES];
+  __shared__ __align__(16) float s_sc0[CFG::SC_FLOATS];
+  uint8_t* s_ops1 = s_ops0;
+  float* s_sc1 = s_sc0;
+#else
   FP8BLK_DECLARE_STAGES(CFG);
+#endif
   __shared__ int64_t s_red[CFG::NT];
   const int64_t per = tiles_m * tiles_n;
   const int64_t lin = blockIdx.x;
@@ -1228,7 +1260,7 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_wgrad(const int32_t* __rest
   t.K = 128 * (pg + ng);
   t.g0 = (int)pg;
   t.g1 = (int)(pg + ng);
-  gemm_tile<CFG, true, true, P2, OM>(t, s_ops0, s_ops1, s_sc0, s_sc1);
+  gemm_tile<CFG, true, true, P2, OM, false, FP8BLK_WGRAD_STAGES == 1>(t, s_ops0, s_ops1, s_sc0, s_sc1);
 }
 
 // Split-K reduction: C[m][n] = sum over s = 0 .. S-1, in that order, of the
