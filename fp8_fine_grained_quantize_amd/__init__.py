@@ -39,6 +39,8 @@ _SIGNATURES = {
     "fp8blk_quantize_1x128": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _u32, _vp]),
     "fp8blk_quantize_128x1": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _u32, _vp]),
     "fp8blk_quantize_block128": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _u32, _vp]),
+    "fp8blk_quantize_1x128_block128": (_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _u32,
+                                              _vp, _i64, _i64, _i64, _vp, _i64, _vp, _u32, _vp]),
     "fp8blk_requantize_128x1_from_1x128": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _u32, _vp]),
     "fp8blk_gemm_fp8_blockscaled": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _int, _vp, _int,
                                            _vp, _i64, _vp, _sz, _vp]),
@@ -211,6 +213,24 @@ def quantize_block128(w: torch.Tensor, pow2: bool = False, q=None, s=None):
     _check(lib().fp8blk_quantize_block128(_ptr(w), R, C, _pitch(w), _ptr(q), _pitch(q), _ptr(s),
                                           SCALE_POW2 if pow2 else 0, _stream()), "quantize_block128")
     return q, s
+
+
+def quantize_1x128_block128(x: torch.Tensor, w: torch.Tensor, pow2_x: bool = False, pow2_w: bool = False,
+                            qx=None, sx=None, qw=None, sw=None):
+    """quantize_1x128(x) and quantize_block128(w) in one launch (the two
+    operands of an Fprop GEMM); returns (qx, sx, qw, sw) as the two calls do."""
+    x, w = _bf16_bits(x), _bf16_bits(w)
+    M, K = x.shape
+    R, C = w.shape
+    qx = _empty_pitched(M, K, torch.uint8, x.device, 1) if qx is None else qx
+    sx = torch.empty((K + 127) // 128, M, dtype=torch.float32, device=x.device) if sx is None else sx
+    qw = _empty_pitched(R, C, torch.uint8, w.device, 1) if qw is None else qw
+    sw = torch.empty((R + 127) // 128, (C + 127) // 128, dtype=torch.float32, device=w.device) if sw is None else sw
+    _check(lib().fp8blk_quantize_1x128_block128(_ptr(x), M, K, _pitch(x), _ptr(qx), _pitch(qx), _ptr(sx),
+                                                SCALE_POW2 if pow2_x else 0, _ptr(w), R, C, _pitch(w), _ptr(qw),
+                                                _pitch(qw), _ptr(sw), SCALE_POW2 if pow2_w else 0, _stream()),
+           "quantize_1x128_block128")
+    return qx, sx, qw, sw
 
 
 def requantize_128x1_from_1x128(q: torch.Tensor, sq: torch.Tensor, pow2: bool = False, qT=None, sT=None):

@@ -11,5 +11,5 @@ extern "C" const char* fp8blk_status_string(fp8blk_status_t status) {
   return "FP8BLK_UNKNOWN_STATUS";
 }
 
-extern "C" int fp8blk_abi_version(void) { return 5; }
+extern "C" int fp8blk_abi_version(void) { return 6; }
 

@@ -56,16 +56,17 @@ __device__ __forceinline__ uint32_t chunk_abs_max(const uint4& v) {
 // ---------------------------------------------------------------------------
 constexpr int Q1_RPL = 2;
 
+// One 1x128 workgroup's work: band `bid` of 16 * Q1_RPL rows x one column
+// group, by 256 lanes numbered `tid`.
 template <bool POW2>
-__global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                      int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-                                                      float* __restrict__ s, int64_t G) {
+__device__ __forceinline__ void quant_1x128_band(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                                                 uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+                                                 int64_t G, int64_t bid, int tid) {
   constexpr int RB = 16 * Q1_RPL;  // rows per workgroup
-  const int64_t bid = blockIdx.x;
   const int64_t g = bid % G;
   const int64_t mb = bid / G;
-  const int sub = threadIdx.x >> 4;
-  const int c16 = threadIdx.x & 15;
+  const int sub = tid >> 4;
+  const int c16 = tid & 15;
   const int64_t col = g * 128 + c16 * 8;
   const int64_t avail = K - col;
 
@@ -89,6 +90,13 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
   }
 }
 
+template <bool POW2>
+__global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                      int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                      float* __restrict__ s, int64_t G) {
+  quant_1x128_band<POW2>(x, M, K, ldx, q, ldq, s, G, blockIdx.x, threadIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // 128x128 blocks, one block per workgroup of NT lanes: lane (sub = tid/16,
 // c16 = tid%16) holds chunk c16 of rows sub, sub + NT/16, ... (2048/NT
@@ -103,14 +111,15 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const uint16_t* __restrict_
 // a kernel with one wave per block and the whole block in registers: 4 %
 // faster at 8064 blocks, 1 % slower at 16384.
 // ---------------------------------------------------------------------------
+// One 128x128 block `blk` (row-major over the block grid) by NT lanes; red
+// is an LDS array of NT/64 words.
 template <bool POW2, int NT>
-__global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restrict__ w, int64_t R, int64_t C,
-                                                        int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ s, int64_t GC) {
+__device__ __forceinline__ void quant_block128_block(const uint16_t* __restrict__ w, int64_t R, int64_t C,
+                                                     int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
+                                                     float* __restrict__ s, int64_t GC, int64_t blk, uint32_t* red) {
   constexpr int CH = 2048 / NT, RSTEP = NT / 16, NWAVE = NT / 64;
-  __shared__ uint32_t red[NWAVE];
   const int sub = threadIdx.x >> 4, c16 = threadIdx.x & 15;
-  const int64_t bi = (int64_t)blockIdx.x / GC, bj = (int64_t)blockIdx.x % GC;
+  const int64_t bi = blk / GC, bj = blk % GC;
   const int64_t col = bj * 128 + c16 * 8;
   const bool interior = (bi + 1) * 128 <= R && (bj + 1) * 128 <= C;
   uint4 v[CH];
@@ -150,6 +159,36 @@ __global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restric
     }
   }
   if (threadIdx.x == 0) s[bi * GC + bj] = ts.s;
+}
+
+template <bool POW2, int NT>
+__global__ __launch_bounds__(NT) void k_quant_block128(const uint16_t* __restrict__ w, int64_t R, int64_t C,
+                                                        int64_t ldw, uint8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ s, int64_t GC) {
+  __shared__ uint32_t red[NT / 64];
+  quant_block128_block<POW2, NT>(w, R, C, ldw, q, ldq, s, GC, blockIdx.x, red);
+}
+
+// Both operands of an Fprop GEMM in one launch: workgroups [0, nW) quantize
+// the weight's 128x128 blocks as above, the rest each take two 1x128 bands of
+// the activation (one per 256-lane half; the 1x128 work has no barrier, so
+// the halves are independent).  One launch instead of two lets the second
+// tensor's loads overlap the first's stores and saves one ramp and tail.
+template <bool P2A, bool P2W>
+__global__ __launch_bounds__(512) void k_quant_pair(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                     int64_t ldx, uint8_t* __restrict__ qx, int64_t ldqx,
+                                                     float* __restrict__ sx, int64_t GA, int64_t nA,
+                                                     const uint16_t* __restrict__ w, int64_t R, int64_t C,
+                                                     int64_t ldw, uint8_t* __restrict__ qw, int64_t ldqw,
+                                                     float* __restrict__ sw, int64_t GC, int64_t nW) {
+  __shared__ uint32_t red[512 / 64];
+  const int64_t b = blockIdx.x;
+  if (b < nW) {
+    quant_block128_block<P2W, 512>(w, R, C, ldw, qw, ldqw, sw, GC, b, red);
+  } else {
+    const int64_t band = (b - nW) * 2 + (threadIdx.x >> 8);
+    if (band < nA) quant_1x128_band<P2A>(x, M, K, ldx, qx, ldqx, sx, GA, band, threadIdx.x & 255);
+  }
 }
 
 
@@ -593,6 +632,36 @@ extern "C" fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R
   else
     hipLaunchKernelGGL((k_quant_block128<false, NT>), dim3((unsigned)blocks), dim3(NT), 0, as_stream(stream), w, R, C,
                        ldw, q, ldq, s, GC);
+  return launch_status();
+}
+
+extern "C" fp8blk_status_t fp8blk_quantize_1x128_block128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                                          uint8_t* qx, int64_t ldqx, float* sx, uint32_t xflags,
+                                                          const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
+                                                          uint8_t* qw, int64_t ldqw, float* sw, uint32_t wflags,
+                                                          void* stream) {
+  if ((xflags | wflags) & ~FP8BLK_SCALE_POW2) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(x, M, K, ldx, 2) || !matrix_ok(qx, M, K, ldqx, 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (!matrix_ok(w, R, C, ldw, 2) || !matrix_ok(qw, R, C, ldqw, 1)) return FP8BLK_ERR_INVALID_ARG;
+  const int64_t GA = ceil_div(K, 128), GR = ceil_div(R, 128), GC = ceil_div(C, 128);
+  if (!vec_ok(sx, GA * M) || !vec_ok(sw, GR * GC)) return FP8BLK_ERR_INVALID_ARG;
+  const bool xa = M > 0 && K > 0, wa = R > 0 && C > 0;
+  if (!xa && !wa) return FP8BLK_OK;
+  if (!xa) return fp8blk_quantize_block128(w, R, C, ldw, qw, ldqw, sw, wflags, stream);
+  if (!wa) return fp8blk_quantize_1x128(x, M, K, ldx, qx, ldqx, sx, xflags, stream);
+  const int64_t nA = ceil_div(M, 16 * Q1_RPL) * GA, nW = GR * GC;
+  const int64_t blocks = nW + ceil_div(nA, (int64_t)2);
+  if (blocks > 0x7FFFFFFF) return FP8BLK_ERR_UNSUPPORTED;
+  const bool pa = (xflags & FP8BLK_SCALE_POW2) != 0, pw = (wflags & FP8BLK_SCALE_POW2) != 0;
+#define FP8BLK_PAIR_LAUNCH(PA, PW)                                                                                \
+  hipLaunchKernelGGL((k_quant_pair<PA, PW>), dim3((unsigned)blocks), dim3(512), 0, as_stream(stream), x, M, K, ldx, \
+                     qx, ldqx, sx, GA, nA, w, R, C, ldw, qw, ldqw, sw, GC, nW)
+  if (pa) {
+    if (pw) FP8BLK_PAIR_LAUNCH(true, true); else FP8BLK_PAIR_LAUNCH(true, false);
+  } else {
+    if (pw) FP8BLK_PAIR_LAUNCH(false, true); else FP8BLK_PAIR_LAUNCH(false, false);
+  }
+#undef FP8BLK_PAIR_LAUNCH
   return launch_status();
 }
 

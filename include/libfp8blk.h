@@ -141,6 +141,21 @@ fp8blk_status_t fp8blk_quantize_block128(const uint16_t* w, int64_t R, int64_t C
                                          void* stream);
 
 /*
+ * Both operands of an Fprop GEMM in one launch: exactly
+ *   fp8blk_quantize_1x128(x, M, K, ldx, qx, ldqx, sx, xflags) and
+ *   fp8blk_quantize_block128(w, R, C, ldw, qw, ldqw, sw, wflags)
+ * (same arguments, layouts and results, bit for bit), with the two
+ * tensors' tiles in one grid so that one launch ramp and tail serve both.
+ * The four outputs must not overlap each other or the inputs.  Either
+ * tensor may be empty (then only the other is quantized).
+ */
+fp8blk_status_t fp8blk_quantize_1x128_block128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                               uint8_t* qx, int64_t ldqx, float* sx, uint32_t xflags,
+                                               const uint16_t* w, int64_t R, int64_t C, int64_t ldw,
+                                               uint8_t* qw, int64_t ldqw, float* sw, uint32_t wflags,
+                                               void* stream);
+
+/*
  * Re-quantization of a cached 1x128-quantized activation into transposed
  * 128x1 tiles: read, dequantize, transpose, re-quantize, store [p5¶4].
  *   q   [T][C] E4M3 codes from fp8blk_quantize_1x128 (pitch ldq >= C),
@@ -354,9 +369,10 @@ size_t fp8blk_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G);
 /* Human-readable name of a status code (static string). */
 const char* fp8blk_status_string(fp8blk_status_t status);
 
-/* ABI version of this header: 5 (2 added the MoE backward entry points, 3 the
+/* ABI version of this header: 6 (2 added the MoE backward entry points, 3 the
  * BF16 output flag and the quantize-on-store GEMM, 4 the matrix-core probe
- * and the allocation-free GEMM, 5 the streaming probe). */
+ * and the allocation-free GEMM, 5 the streaming probe, 6 the two-operand
+ * quantizer). */
 int fp8blk_abi_version(void);
 
 #ifdef __cplusplus

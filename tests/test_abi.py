@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fb.abi_version() == 5
+    assert fb.abi_version() == 6
     assert fb.token_group_slots(65536, 256) == 512 + 256
     assert fb.token_group_slots(100, 3) == 3 and fb.token_group_slots(-1, 3) == 0
     assert fb.status_string(0) == "FP8BLK_OK"
@@ -83,6 +83,21 @@ def test_quantizer_validation(fn):
     # empty shapes are valid no-ops (nothing enqueued)
     assert f(NULL, 0, 128, 128, NULL, 128, NULL, 0, NULL) == OK
     assert f(NULL, 4, 0, 128, NULL, 128, NULL, 0, NULL) == OK
+
+
+def test_two_operand_quantizer_validation():
+    f = fb.lib().fp8blk_quantize_1x128_block128
+    good = (FAKE, 4, 128, 128, FAKE, 128, FAKE, 0)  # valid on its own; never passed with a valid partner
+    # each side's arguments are checked as by its own entry point
+    assert f(NULL, 4, 128, 128, FAKE, 128, FAKE, 0, *good, NULL) == INVALID
+    assert f(*good, FAKE, 4, 128, 128, FAKE, 128, NULL, 0, NULL) == INVALID
+    assert f(FAKE, 4, 128, 120, FAKE, 128, FAKE, 0, *good, NULL) == INVALID
+    assert f(*good, FAKE, 4, 128, 128, FAKE, 112, FAKE, 0, NULL) == INVALID
+    assert f(FAKE, 4, 128, 128, FAKE, 128, FAKE, 0x2, *good, NULL) == INVALID
+    assert f(*good, FAKE, 4, 128, 128, FAKE, 128, FAKE, 0x4, NULL) == INVALID
+    assert f(MIS, 4, 128, 128, FAKE, 128, FAKE, 0, *good, NULL) == INVALID
+    # both empty: a valid no-op
+    assert f(NULL, 0, 128, 128, NULL, 128, NULL, 0, NULL, 4, 0, 128, NULL, 128, NULL, 0, NULL) == OK
 
 
 def test_requantize_validation():

@@ -158,6 +158,44 @@ def test_requantize_wide_range_and_subnormal_scales(pow2):
     assert np.array_equal(np_f32(sT).view(np.uint32), sTo.view(np.uint32))
 
 
+@pytest.mark.parametrize("pow2_x,pow2_w", [(False, False), (True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("xshape,wshape", [((300, 520), (130, 140)), ((10, 100), (7168, 4096)),
+                                           ((4096, 7168), (257, 384)), ((33, 129), (1, 8))])
+def test_two_operand_quantizer(xshape, wshape, pow2_x, pow2_w):
+    """quantize_1x128_block128 equals the two separate quantizers bit for bit
+    (an odd number of 1x128 bands leaves half a workgroup idle), and the
+    oracle on every code and scale."""
+    g = torch.Generator().manual_seed(xshape[0] + wshape[1])
+    x = synthetic.randn_bf16(xshape, 1.0, g, outlier_cols=2, outlier_factor=30.0)
+    w = synthetic.randn_bf16(wshape, 0.02, g)
+    print(f"[quant] two-operand x={xshape} w={wshape} pow2={pow2_x},{pow2_w}", flush=True)
+    qx, sx, qw, sw = fb.quantize_1x128_block128(dev(x), dev(w), pow2_x, pow2_w)
+    qx1, sx1 = fb.quantize_1x128(dev(x), pow2=pow2_x)
+    qw1, sw1 = fb.quantize_block128(dev(w), pow2=pow2_w)
+    torch.cuda.synchronize()
+    assert torch.equal(qx, qx1) and torch.equal(sx, sx1) and torch.equal(qw, qw1) and torch.equal(sw, sw1)
+    if xshape[0] * xshape[1] <= 300 * 520:
+        qo, so = oracle.quantize_1x128(bf16_bits(x), pow2_x)
+        assert np.array_equal(np_u8(qx), qo) and np.array_equal(np_f32(sx).view(np.uint32), so.view(np.uint32))
+    if wshape[0] * wshape[1] <= 257 * 384:
+        qo, so = oracle.quantize_block128(bf16_bits(w), pow2_w)
+        assert np.array_equal(np_u8(qw), qo) and np.array_equal(np_f32(sw).view(np.uint32), so.view(np.uint32))
+
+
+def test_two_operand_quantizer_one_side_empty():
+    g = torch.Generator().manual_seed(3)
+    x = synthetic.randn_bf16((64, 256), 1.0, g)
+    w = synthetic.randn_bf16((256, 128), 0.02, g)
+    e = torch.empty(0, 256, dtype=torch.bfloat16)
+    qx, sx, qw, sw = fb.quantize_1x128_block128(dev(x), dev(e))
+    qx1, sx1 = fb.quantize_1x128(dev(x))
+    qx2, sx2, qw2, sw2 = fb.quantize_1x128_block128(dev(e), dev(w))
+    qw1, sw1 = fb.quantize_block128(dev(w))
+    torch.cuda.synchronize()
+    assert torch.equal(qx, qx1) and torch.equal(sx, sx1) and qw.shape == (0, 256)
+    assert torch.equal(qw2, qw1) and torch.equal(sw2, sw1) and qx2.shape == (0, 256)
+
+
 def test_empty_inputs_are_noops():
     x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
     q, s = fb.quantize_1x128(x)
