@@ -241,9 +241,8 @@ __global__ __launch_bounds__(256) void k_quant_128x1(const uint16_t* __restrict_
   int64_t t0 = (int64_t)blockIdx.y * 128, t_end = T;
   int64_t o0 = t0, o_end = T;
   if (GROUPED) {
-    __shared__ int64_t sh_scan[257], sh_found[2];
     int64_t e, local;
-    token_group_owner<256>(off, G, blockIdx.y, sh_scan, sh_found, e, local);
+    token_group_owner(off, G, blockIdx.y, e, local);
     if (e < 0) return;  // uniform across the block
     t0 = (int64_t)off[e] + 128 * local;
     t_end = off[e + 1];
