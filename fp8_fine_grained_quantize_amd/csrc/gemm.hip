@@ -1127,49 +1127,39 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
                                                            int64_t stride_sB, int64_t sB_ld,
                                                            void* __restrict__ C, int64_t ldc, int64_t tiles_n) {
   FP8BLK_DECLARE_STAGES(CFG);
-  __shared__ int64_t s_tile_base[CFG::NT + 1];
-  __shared__ int64_t s_found[2];
   const int tid = threadIdx.x;
   // Linear tile id with the XCD remap.
   const int64_t nblocks = gridDim.x;
   int64_t lin = blockIdx.x;
   if (nblocks % 8 == 0) lin = (lin % 8) * (nblocks / 8) + lin / 8;
 
-  // Walk the experts in chunks of NT: each thread counts one expert's tiles,
-  // an LDS prefix sum locates the expert that owns tile `lin`.
-  int64_t base = 0;
-  if (tid == 0) s_found[0] = -1;
-  for (int64_t e0 = 0; e0 < G; e0 += CFG::NT) {
-    const int64_t e = e0 + tid;
-    int64_t cnt = 0;
-    if (e < G) {
-      const int64_t rows = (int64_t)offsets[e + 1] - (int64_t)offsets[e];
-      cnt = ((rows + CFG::BM - 1) / CFG::BM) * tiles_n;
+  // Find the expert that owns tile `lin`: each wave walks the experts 64 at a
+  // time, one per lane, with an inclusive scan of their tile counts (lane
+  // exchanges only; every wave reaches the same answer).  The grid is below
+  // 2^31 workgroups, so the counts fit 32 bits.
+  int64_t e = -1, local = 0;
+  {
+    const int lane = tid & 63;
+    int64_t base = 0;
+    for (int64_t e0 = 0; e0 < G; e0 += 64) {
+      const int64_t ee = e0 + lane;
+      int32_t cnt = 0;
+      if (ee < G) {
+        const int64_t rows = (int64_t)offsets[ee + 1] - (int64_t)offsets[ee];
+        cnt = (int32_t)(((rows + CFG::BM - 1) / CFG::BM) * tiles_n);
+      }
+      const int32_t incl = wave_inclusive_sum(cnt);
+      const int64_t lo = base + incl - cnt;
+      const uint64_t who = __ballot(ee < G && lin >= lo && lin < base + incl);
+      if (who) {
+        const int src = __ffsll((unsigned long long)who) - 1;
+        e = wave_uniform(e0 + src);
+        local = wave_uniform(lin - __shfl(lo, src));
+        break;
+      }
+      base = wave_uniform(base + __shfl(incl, 63));
     }
-    __syncthreads();
-    s_tile_base[tid + 1] = cnt;
-    if (tid == 0) s_tile_base[0] = 0;
-    __syncthreads();
-    // inclusive scan (Hillis-Steele) of entries 1..NT; entry 0 stays 0
-    for (int d = 1; d <= CFG::NT; d <<= 1) {
-      const int64_t v = (tid + 1 - d >= 0) ? s_tile_base[tid + 1 - d] : 0;
-      __syncthreads();
-      if (tid + 1 - d >= 0) s_tile_base[tid + 1] += v;
-      __syncthreads();
-    }
-    const int64_t lo = base + s_tile_base[tid];
-    const int64_t hi = base + s_tile_base[tid + 1];
-    if (e < G && lin >= lo && lin < hi) {
-      s_found[0] = e;
-      s_found[1] = lin - lo;
-    }
-    const int64_t chunk_total = s_tile_base[CFG::NT];
-    __syncthreads();
-    if (s_found[0] >= 0) break;
-    base += chunk_total;
   }
-  const int64_t e = s_found[0];
-  const int64_t local = s_found[1];
   if (e < 0) return;  // surplus workgroup (uniform across the block)
   const int64_t r0 = offsets[e];
   const int64_t rows_e = (int64_t)offsets[e + 1] - r0;
