@@ -1115,8 +1115,9 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
 // Grouped: tiles are enumerated expert by expert, within an expert column
 // tile by column tile, row tiles innermost, so that concurrently running
 // workgroups share each expert's weight tile.  The per-expert row counts are
-// read from the device-resident offsets (prefix scan in LDS), so the host
-// never synchronizes; surplus workgroups of the upper-bound grid exit.
+// read from the device-resident offsets (a wave-level scan of the experts' tile
+// counts), so the host never synchronizes; surplus workgroups of the
+// upper-bound grid exit.
 template <class CFG, bool OPB_T, bool P2, int OM>
 __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32_t* __restrict__ offsets,
                                                            int64_t M_total, int64_t N, int64_t K,
