@@ -62,23 +62,32 @@ struct TileCfg {
   static constexpr int BM = WAVES_M * WTM, BN = WAVES_N * WTN;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int A_CHUNKS = A_BYTES / 16, B_CHUNKS = B_BYTES / 16;
-  static constexpr int A_ITERS = A_CHUNKS / (64 * NW), B_ITERS = B_CHUNKS / (64 * NW);
-  // Scale copies: BM floats of sA then BN floats of sB-side scales, 64
-  // floats per wave instruction, one instruction per wave.
-  static constexpr int S_BLOCKS = (BM + BN) / 64;
+  // Copy iterations of 1 KB per wave; the last A iteration is partial when
+  // BM is not a multiple of 8 * NW rows (only its first waves copy).
+  static constexpr int A_ITERS = (A_CHUNKS + 64 * NW - 1) / (64 * NW), B_ITERS = B_CHUNKS / (64 * NW);
+  static constexpr bool A_PARTIAL = A_CHUNKS % (64 * NW) != 0;
+  // Scale copies: row scales of sA then BN floats of sB-side scales, 64
+  // floats per wave instruction, one instruction per wave.  A lane's row
+  // scales are a run of TMP = TM rounded up to 4 floats (read as float4), so
+  // the row part holds BMP = WAVES_M * 16 * TMP floats (BM when TM % 4 == 0).
+  static constexpr int TMP = (TM + 3) / 4 * 4, WTMP = 16 * TMP, BMP = WAVES_M * WTMP;
+  static constexpr int S_BLOCKS = (BMP + BN) / 64;
   static constexpr int BUF_BYTES = A_BYTES + B_BYTES;
-  static constexpr int SC_FLOATS = BM + BN;
+  static constexpr int SC_FLOATS = BMP + BN;
   static constexpr int LDS_BYTES = 2 * (BUF_BYTES + SC_FLOATS * 4);
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns must lie in one 128-column scale block");
   static_assert(BN >= 128, "the N-major swizzle needs BN >= 128");
-  static_assert(A_CHUNKS % (64 * NW) == 0 && B_CHUNKS % (64 * NW) == 0, "whole 1 KB copy blocks per wave");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "scale copies in 64-float blocks");
+  static_assert(A_CHUNKS % 64 == 0 && B_CHUNKS % (64 * NW) == 0, "whole 1 KB copy blocks per wave");
+  static_assert(BMP % 64 == 0 && BN % 64 == 0, "scale copies in 64-float blocks");
   static_assert(S_BLOCKS <= NW, "one scale copy per wave");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
 };
 
 #ifndef FP8BLK_BIG_CFG
 #define FP8BLK_BIG_CFG 2, 4, 8, 4  // 256 x 256 tile, 8 waves of 128 x 64
+#endif
+#ifndef FP8BLK_BIG224_CFG
+#define FP8BLK_BIG224_CFG 2, 4, 7, 4  // 224 x 256 tile, 8 waves of 112 x 64
 #endif
 #ifndef FP8BLK_SMALL_CFG
 #define FP8BLK_SMALL_CFG 2, 2, 4, 4  // 128 x 128 tile, 4 waves of 64 x 64
@@ -87,6 +96,7 @@ struct TileCfg {
 #define FP8BLK_ROW_CFG 2, 2, 4, 4  // 128 x 128 tile, 4 waves of 64 x 64 (per-column scales need more registers)
 #endif
 using BigCfg = TileCfg<FP8BLK_BIG_CFG>;
+using Big224Cfg = TileCfg<FP8BLK_BIG224_CFG>;
 using SmallCfg = TileCfg<FP8BLK_SMALL_CFG>;
 using RowCfg = TileCfg<FP8BLK_ROW_CFG>;
 
@@ -276,22 +286,25 @@ struct CopyPlan {
   // integer operations per group instead of a VGPR held across the K loop);
   // the row-pipelined loop forms it once per tile.
   __device__ __forceinline__ uint32_t sc_offset(const TileArgs& t) const {
-    constexpr int TM = CFG::TM, WTM = CFG::WTM;
+    constexpr int TMP = CFG::TMP, WTM = CFG::WTM, WTMP = CFG::WTMP, BMP = CFG::BMP;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     int blk = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (blk >= CFG::S_BLOCKS) blk = 0;  // surplus copy: rewrites block 0 with the same data
-    const int p = blk * 64 + lane;      // float position in the [BM + BN] scale buffer
-    // BM is a multiple of 64, so the row/column choice is uniform per wave
+    const int p = blk * 64 + lane;      // float position in the [BMP + BN] scale buffer
+    // BMP is a multiple of 64, so the row/column choice is uniform per wave
     // (derived from blk alone), which keeps the resource in scalar registers.
-    const int w = p / WTM, q = p % WTM;
-    const uint32_t row_off = (uint32_t)((w * WTM + 16 * (q % TM) + q / TM) * 4);
-    // column scale of column n0 + (p - BM), or block scale of column block
-    // n0/128 + (p - BM) (only the first BN/128 positions are used)
+    // Position q of wave row w is lane q / TMP's row tile q % TMP; padding
+    // positions (row tile >= TM) load a row that is never read back (past
+    // the tile's rows it reads as zero).
+    const int w = p / WTMP, q = p % WTMP;
+    const uint32_t row_off = (uint32_t)((w * WTM + 16 * (q % TMP) + q / TMP) * 4);
+    // column scale of column n0 + (p - BMP), or block scale of column block
+    // n0/128 + (p - BMP) (only the first BN/128 positions are used)
     const uint32_t col_off =
-        ROW128 ? (uint32_t)((p - BM) * 4) : (uint32_t)((p - BM) * (OPB_T ? (int)(t.K >> 7) : 1) * 4);
-    if (blk * 64 < BM) return row_off;
+        ROW128 ? (uint32_t)((p - BMP) * 4) : (uint32_t)((p - BMP) * (OPB_T ? (int)(t.K >> 7) : 1) * 4);
+    if (blk * 64 < BMP) return row_off;
     return col_off;
   }
 
@@ -333,6 +346,7 @@ struct CopyPlan {
                                             v4i rsa, v4i rsb, int n,
                                             const TileArgs& t, uint8_t* buf, float* sbuf) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    static_assert(!CFG::A_PARTIAL, "the 128x128 tiles copy whole A iterations");
     if (n < CFG::A_ITERS) {
       const int it = n;
       dma16(ra, a, (int32_t)(it * 8 * NW * t.lda), buf + (it * NW + wave) * 1024);
@@ -342,7 +356,7 @@ struct CopyPlan {
       dma16(rb, (!OPB_T && (it & 1)) ? b2 : b, so, buf + CFG::A_BYTES + (it * NW + wave) * 1024);
     } else {
       const int blk = wave < CFG::S_BLOCKS ? wave : 0;
-      const bool rows = blk * 64 < BM;  // wave-uniform; a select keeps the copy branch-free
+      const bool rows = blk * 64 < CFG::BMP;  // wave-uniform; a select keeps the copy branch-free
       const v4i rs = v4i{rows ? rsa[0] : rsb[0], rows ? rsa[1] : rsb[1], rows ? rsa[2] : rsb[2], rows ? rsa[3] : rsb[3]};
       dma4(rs, sc_offset(t), (uint8_t*)(sbuf + blk * 64));
     }
@@ -350,11 +364,12 @@ struct CopyPlan {
 };
 
 // Whether a tile runs the row-pipelined K loop (gemm_loop_rows below): tiles
-// with ROWPIPE_MIN_TM or more row tiles per wave (the 256x256 tile).  The
+// with ROWPIPE_MIN_TM or more row tiles per wave (the 256x256 and 224x256
+// tiles).  The
 // 128x128 tiles (two workgroups per CU) keep the loop that issues a group's
 // copies at its start (compute_group below).
 #ifndef FP8BLK_ROWPIPE_MIN_TM
-#define FP8BLK_ROWPIPE_MIN_TM 8
+#define FP8BLK_ROWPIPE_MIN_TM 7
 #endif
 template <class CFG, bool ROW128>
 constexpr bool row_pipelined() { return CFG::TM >= FP8BLK_ROWPIPE_MIN_TM; }
@@ -398,7 +413,7 @@ __device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s
 template <class CFG, bool OPB_T, bool ROW128, bool P2>
 __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* sc,
                                               v4f (&acc)[CFG::TM][CFG::TN]) {
-  constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
+  constexpr int BN = CFG::BN, TM = CFG::TM, TN = CFG::TN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -408,10 +423,10 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
   const uint8_t* Bs = ops + CFG::A_BYTES;
 
   // Row scales of this lane's TM row tiles (contiguous by the copy plan).
-  float sa[TM];
+  float sa[CFG::TMP];
 #pragma unroll
   for (int i = 0; i < TM; i += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
+    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTMP + l16 * CFG::TMP + i);
     sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
   }
   // Column scales: one block value per wave, or four per column tile.
@@ -419,9 +434,9 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
   float sbb = 0.0f;
   if (ROW128) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sc + BM + wn * CFG::WTN + 16 * j + 4 * lq);
+    for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sc + CFG::BMP + wn * CFG::WTN + 16 * j + 4 * lq);
   } else {
-    sbb = sc[BM + (wn * CFG::WTN) / 128];
+    sbb = sc[CFG::BMP + (wn * CFG::WTN) / 128];
   }
 
   // B fragments of this wave's TN column tiles.
@@ -470,7 +485,7 @@ __device__ __forceinline__ void compute_group(const uint8_t* ops, const float* s
     if (ROW128) {
 #pragma unroll
       for (int j = 0; j < TN && j < 4; ++j)
-        sbe |= e8m0_of(sc[BM + wn * CFG::WTN + 16 * j + l16]) << (8 * j);
+        sbe |= e8m0_of(sc[CFG::BMP + wn * CFG::WTN + 16 * j + l16]) << (8 * j);
     } else {
       sbe = e8m0_of(sbb);
     }
@@ -618,7 +633,10 @@ __device__ __forceinline__ void issue_copies(const TileArgs& t, const CopyPlan<C
 #pragma unroll
   for (int n = n0; n < n1; ++n) {
     if (n < CFG::A_ITERS) {
-      if constexpr (SKIP)
+      // The partial last iteration of a BM that is not a multiple of 8 * NW
+      // rows: a wave whose 8 rows start at or past the tile's valid rows
+      // (t.rows <= BM) issues nothing, so no copy lands beyond the A tile.
+      if (SKIP || (CFG::A_PARTIAL && n == CFG::A_ITERS - 1))
         dma16_if(ra, plan.a, (int32_t)(n * 8 * NW * t.lda), buf + (n * NW + wave) * 1024,
                  (int32_t)t.rows - (n * NW + wave) * 8);
       else
@@ -640,7 +658,7 @@ __device__ __forceinline__ void compute_group_rows(const uint8_t* ops, const flo
                                                    const TileArgs& t, const CopyPlan<CFG, OPB_T, ROW128>& plan,
                                                    uint32_t scoff, const v4i& ra, const v4i& rb, const v4i& rs,
                                                    uint8_t* nops, float* nsc, int wave, int blk) {
-  constexpr int BM = CFG::BM, BN = CFG::BN, TM = CFG::TM, TN = CFG::TN, R = FP8BLK_FOLD_RING;
+  constexpr int BN = CFG::BN, TM = CFG::TM, TN = CFG::TN, R = FP8BLK_FOLD_RING;
   constexpr int LOADS = CopyPlan<CFG, OPB_T, ROW128>::LOADS, CR = FP8BLK_COPY_ROWS;
   static_assert(CR >= 1 && CR <= TM, "copy rows");
   const int lane = threadIdx.x & 63;
@@ -677,19 +695,19 @@ __device__ __forceinline__ void compute_group_rows(const uint8_t* ops, const flo
   }
   // Row scales of this lane's row tiles, and the wave's block scale or (ROW128)
   // the column scales of its column tiles.
-  float sa[TM];
+  float sa[CFG::TMP];
 #pragma unroll
   for (int i = 0; i < TM; i += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTM + l16 * TM + i);
+    const float4 v = *reinterpret_cast<const float4*>(sc + wm * CFG::WTMP + l16 * CFG::TMP + i);
     sa[i] = v.x; sa[i + 1] = v.y; sa[i + 2] = v.z; sa[i + 3] = v.w;
   }
   float sbb = 0.0f;
   float4 sbv[ROW128 ? TN : 1];
   if constexpr (ROW128) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sc + BM + wn * CFG::WTN + 16 * j + 4 * lq);
+    for (int j = 0; j < TN; ++j) sbv[j] = *reinterpret_cast<const float4*>(sc + CFG::BMP + wn * CFG::WTN + 16 * j + 4 * lq);
   } else {
-    sbb = sc[BM + (wn * CFG::WTN) / 128];
+    sbb = sc[CFG::BMP + (wn * CFG::WTN) / 128];
   }
 
   if constexpr (P2) {
@@ -704,7 +722,7 @@ __device__ __forceinline__ void compute_group_rows(const uint8_t* ops, const flo
     uint32_t sbe = 0;
     if constexpr (ROW128) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sbe |= e8m0_of(sc[BM + wn * CFG::WTN + 16 * j + l16]) << (8 * j);
+      for (int j = 0; j < TN; ++j) sbe |= e8m0_of(sc[CFG::BMP + wn * CFG::WTN + 16 * j + l16]) << (8 * j);
     } else {
       sbe = e8m0_of(sbb);
     }
@@ -780,7 +798,7 @@ __device__ __forceinline__ void gemm_loop_rows(const TileArgs& t, uint8_t* ops0,
   plan.init(t);
   const uint32_t scoff = plan.sc_offset(t);
   GroupCursor<CFG, OPB_T, ROW128> cur;
-  cur.init(t, g0, blk * 64 < CFG::BM);
+  cur.init(t, g0, blk * 64 < CFG::BMP);
   if (g0 < G)  // no groups (an expert without tokens): C = 0
     issue_copies<CFG, OPB_T, ROW128, SKIP>(t, plan, scoff, cur.ra(true), cur.rb(true), cur.rs(true), 0,
                              CopyPlan<CFG, OPB_T, ROW128>::LOADS, ops0, sc0, wave, blk);
@@ -1315,6 +1333,23 @@ static int64_t splitk_count(int64_t M, int64_t N, int64_t K) {
   return S < 1 ? 1 : S;
 }
 
+// 224x256 tiles in place of 256x256 when they take fewer tile rows per CU:
+// ceil(tiles / CUs) launch waves times the tile height.  On 256 CUs the
+// 7168 x 2048 output (the Wgrad of a 7168-wide layer over a 2048-wide one)
+// is 224 tiles of 256 rows, one launch wave with 32 CUs idle, or exactly 256
+// tiles of 224 rows, each 7/8 of the MFMA work and 15/16 of the copies;
+// square outputs such as 4096 x 4096 keep the 256-row tiles.  Measured
+// (interleaved against 256-row tiles, one box, results bitwise identical):
+// 7168 x 2048 x 4096 Wgrad 77.0 -> 73.8 us, power-of-two scales 70.8 -> 67.8;
+// 4100 x 2050 x 7168 (153 -> 171 tiles) 104.5 -> 97.4 us, power-of-two
+// 98.7 -> 101.6 (the one loss).
+static bool use_tile224(int64_t M, int64_t N) {
+  const int64_t cus = device_cus();
+  const int64_t t256 = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
+  const int64_t t224 = ceil_div(M, Big224Cfg::BM) * ceil_div(N, Big224Cfg::BN);
+  return ceil_div(t224, cus) * Big224Cfg::BM < ceil_div(t256, cus) * BigCfg::BM;
+}
+
 static size_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t S = splitk_count(M, N, K);
   const int64_t Np = (N + 3) & ~int64_t(3);
@@ -1418,14 +1453,19 @@ static fp8blk_status_t gemm_dense(int64_t M, int64_t N, int64_t K, const uint8_t
     else
       S = 1;
   }
-  // 256x256 tiles when they give at least half a wave of workgroups over
-  // the 256 CUs, 128x128 tiles otherwise.
+  // 256x256 tiles (or 224x256, see use_tile224) when they give at least
+  // half a wave of workgroups over the 256 CUs, 128x128 tiles otherwise.
   const int64_t big_tiles = ceil_div(M, BigCfg::BM) * ceil_div(N, BigCfg::BN);
+  const bool t224 = big_tiles >= 128 && use_tile224(M, N);
   if (bscale_mode == FP8BLK_BSCALE_ROW128) {
+    if (t224)
+      return dispatch_dense<Big224Cfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
     if (big_tiles >= 128)
       return dispatch_dense<BigCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
     return dispatch_dense<SmallCfg, true>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   }
+  if (t224)
+    return dispatch_dense<Big224Cfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   if (big_tiles >= 128)
     return dispatch_dense<BigCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);
   return dispatch_dense<SmallCfg, false>(t, p2, M, N, K, A, lda, sA, B, ldb, sB, sB_ld, C, ldc, ob, partials, S, st);

@@ -93,8 +93,10 @@ def test_exact_small_integers_bitwise(opB, mode):
 @pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("opB,mode", CASES)
 def test_exact_small_integers_bitwise_256x256_tiles(opB, mode, pow2):
-    """The same exact case on a shape whose 256 x 256 tiles fill the GPU (the
-    row-pipelined loop), fold and power-of-two paths, with ragged edges."""
+    """The same exact case on a shape whose big tiles fill the GPU (the
+    row-pipelined loop; at 4100 x 2050 on 256 CUs the 224 x 256 tiles, the
+    256 x 256 ones are covered in test_gpu_gemm_tiles.py), fold and
+    power-of-two paths, with ragged edges."""
     rng = np.random.default_rng(13)
     M, N, K = 4100, 2050, 384
     G = K // 128
