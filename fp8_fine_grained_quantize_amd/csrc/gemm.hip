@@ -1124,11 +1124,18 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
 // are not issued.  Measured (interleaved, one box, bitwise identical): MoE
 // up 3.26 -> 3.23 ms, down 2.055 -> 2.025 ms, down Dgrad 1.69 -> 1.68 ms.
 // An L2 prefetch of each tile's weight slab 2-4 groups ahead (4-byte copies
-// into a dummy LDS area) made all three 10-13 % slower and was dropped: the
-// grouped tiles run within about 17 % of the dense tiles' time per tile, so
-// the weight stream's latency is not what bounds them.
+// into a dummy LDS area) made all three 10-13 % slower and was dropped.
+// Balancing the real tiles over the 8 XCDs (FP8BLK_GROUPED_BALANCE, in place
+// of a remap over the whole upper-bound grid, which left the MoE shapes'
+// tiles to six XCDs, 1.27x the balanced share on the busiest): MoE up 3.35 ->
+// 2.94 ms, down 2.15 -> 1.81 ms, down Dgrad 1.72 -> 1.45 ms (interleaved, one
+// box, bitwise identical), so a grouped tile now takes within a few percent of
+// a dense tile's time (2.94 ms over 25.2 tiles per CU).
 #ifndef FP8BLK_GROUPED_SKIP
 #define FP8BLK_GROUPED_SKIP 1
+#endif
+#ifndef FP8BLK_GROUPED_BALANCE
+#define FP8BLK_GROUPED_BALANCE 1
 #endif
 // Grouped: tiles are enumerated expert by expert, within an expert column
 // tile by column tile, row tiles innermost, so that concurrently running
@@ -1147,26 +1154,44 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
                                                            void* __restrict__ C, int64_t ldc, int64_t tiles_n) {
   FP8BLK_DECLARE_STAGES(CFG);
   const int tid = threadIdx.x;
-  // Linear tile id with the XCD remap.
+  const int lane = tid & 63;
+  // Tiles of an expert: its row tiles times the column tiles.  The grid is
+  // below 2^31 workgroups and covers every tile, so the counts fit 32 bits.
+  auto expert_tiles = [&](int64_t ee) -> int32_t {
+    if (ee >= G) return 0;
+    const int64_t rows = (int64_t)offsets[ee + 1] - (int64_t)offsets[ee];
+    return (int32_t)(((rows + CFG::BM - 1) / CFG::BM) * tiles_n);
+  };
+#if FP8BLK_GROUPED_BALANCE
+  // Workgroups are dealt to the 8 XCDs round-robin: workgroup b runs on XCD
+  // b % 8, as that XCD's (b / 8)-th.  XCD x takes the contiguous run
+  // [x * per, (x + 1) * per) of the `total` real tiles, so that the XCDs get
+  // equal shares and one XCD's workgroups share each expert's weight and
+  // activation panels through its L2.  (The grid is an upper bound padded to
+  // a multiple of 8; remapping over the whole grid left the real tiles to
+  // the first six XCDs of the MoE shapes.)
+  int64_t total = 0;
+  for (int64_t e0 = 0; e0 < G; e0 += 64)
+    total = wave_uniform(total + __shfl(wave_inclusive_sum(expert_tiles(e0 + lane)), 63));
+  const int64_t per = (total + 7) / 8, slot = blockIdx.x / 8;
+  if (slot >= per) return;  // surplus workgroup (uniform across the block)
+  const int64_t lin = (int64_t)(blockIdx.x % 8) * per + slot;
+  if (lin >= total) return;
+#else
   const int64_t nblocks = gridDim.x;
   int64_t lin = blockIdx.x;
   if (nblocks % 8 == 0) lin = (lin % 8) * (nblocks / 8) + lin / 8;
+#endif
 
   // Find the expert that owns tile `lin`: each wave walks the experts 64 at a
   // time, one per lane, with an inclusive scan of their tile counts (lane
-  // exchanges only; every wave reaches the same answer).  The grid is below
-  // 2^31 workgroups, so the counts fit 32 bits.
+  // exchanges only; every wave reaches the same answer).
   int64_t e = -1, local = 0;
   {
-    const int lane = tid & 63;
     int64_t base = 0;
     for (int64_t e0 = 0; e0 < G; e0 += 64) {
       const int64_t ee = e0 + lane;
-      int32_t cnt = 0;
-      if (ee < G) {
-        const int64_t rows = (int64_t)offsets[ee + 1] - (int64_t)offsets[ee];
-        cnt = (int32_t)(((rows + CFG::BM - 1) / CFG::BM) * tiles_n);
-      }
+      const int32_t cnt = expert_tiles(ee);
       const int32_t incl = wave_inclusive_sum(cnt);
       const int64_t lo = base + incl - cnt;
       const uint64_t who = __ballot(ee < G && lin >= lo && lin < base + incl);
@@ -1591,8 +1616,8 @@ extern "C" fp8blk_status_t fp8blk_grouped_gemm_fp8_blockscaled(
   // 128-row tiles (64 % against 79 % useful rows), but each group's copies
   // feed four times the MFMA work, and the copies, not the matrix cores,
   // bound these kernels: measured against 128 x 128 tiles (interleaved, one
-  // box, bitwise identical) MoE up 3.32 / 3.50 ms, down 2.08 / 2.16 ms, down
-  // Dgrad 1.72 / 1.71 ms.
+  // box, bitwise identical, both before the XCD balance of the kernel) MoE
+  // up 3.32 / 3.50 ms, down 2.08 / 2.16 ms, down Dgrad 1.72 / 1.71 ms.
   using CFG = BigCfg;
   if (G < 0 || M_total < 0 || N < 0 || K < 0 || max_group_rows < 0) return FP8BLK_ERR_INVALID_ARG;
   const bool p2 = (opB & FP8BLK_GEMM_POW2_SCALES) != 0;
