@@ -49,8 +49,8 @@ QUANT_BYTES_BLOCK = 2 + 1 + 4 / (128 * 128)
 # of its 4 x 8 block of tiles once (8 x 12 x 1.84 MB); sharing across XCDs is
 # left to the Infinity Cache.  Valid only for the GEMM source it was measured
 # on (sha256 below); reported as null otherwise.
-GEMM_TRAFFIC = {"sha256": "60e087ef03e1e1f15ef2fde6585e7ebb79efa79df526a22206ce11d3555ae7af",
-                "fetch_bytes": 178243169, "write_bytes": 67108864}
+GEMM_TRAFFIC = {"sha256": "0f598efa1b53ec9cfecedf3f112db8ad87386b2991bb884a7e489a004343ee07",
+                "fetch_bytes": 178242636, "write_bytes": 67108872}
 
 
 def parse():
