@@ -55,6 +55,43 @@ def test_grouped_small(opB, counts):
         assert np.array_equal(np_f32(Cd).view(np.uint32), Cg[r0:r1].view(np.uint32)), f"expert {e}"
 
 
+@pytest.mark.parametrize("G", [63, 64, 65, 256, 257, 300])
+def test_grouped_many_experts(G):
+    """Expert counts around the 64-expert chunks of the kernel's tile lookup
+    and past the 256 experts whose tile counts it keeps in registers (beyond
+    them it walks the offsets chunk by chunk): the oracle gate over the whole
+    output and bit equality with one dense call per expert."""
+    print(f"[grouped] {G} experts", flush=True)
+    K, N = 256, 144
+    rng = np.random.default_rng(G)
+    counts = rng.integers(0, 24, size=G)
+    counts[rng.integers(0, G, size=3)] = [0, 300, 257]  # some empty, two spanning several row tiles
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    Mt = int(off[-1])
+    g = torch.Generator().manual_seed(G)
+    A = synthetic.randn_bf16((Mt, K), 1.0, g)
+    qA, sA = oracle.quantize_1x128(bf16_bits(A))
+    W = synthetic.randn_bf16((G * K, N), 0.02, g)
+    qW, sW = oracle.quantize_block128(bf16_bits(W))      # the experts' [K][N] weights stacked
+    B = qW.reshape(G, K, N)
+    sB = sW.reshape(G, K // 128, -1)
+    offs = torch.from_numpy(off.astype(np.int32)).cuda()
+    C = fb.grouped_gemm_fp8_blockscaled(offs, u8_dev(qA), f32_dev(sA), u8_dev(B), f32_dev(sB))
+    torch.cuda.synchronize()
+    Cg = np_f32(C)
+    R = oracle.grouped_gemm_blockscaled(off, qA, sA, B, sB, oracle.OP_N)
+    assert e_norm(Cg, R) <= 1e-3
+    dA, dsA = u8_dev(qA), f32_dev(sA)
+    for e in range(G):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        Cd = fb.gemm_fp8_blockscaled(dA[r0:r1], dsA[:, r0:r1].contiguous(), u8_dev(B[e]), f32_dev(sB[e]),
+                                     split_k=False)
+        torch.cuda.synchronize()
+        assert np.array_equal(np_f32(Cd).view(np.uint32), Cg[r0:r1].view(np.uint32)), f"expert {e}"
+
+
 def test_moe_up_projection_sampled():
     """256 experts, top-8 of 8192 tokens, K=7168 -> N=4096, weights drawn on
     the device per expert; X quantized 1x128 with power-of-two scales before
