@@ -1125,17 +1125,14 @@ __global__ __launch_bounds__(CFG::NT) void k_gemm(int64_t M, int64_t N, int64_t 
 // up 3.26 -> 3.23 ms, down 2.055 -> 2.025 ms, down Dgrad 1.69 -> 1.68 ms.
 // An L2 prefetch of each tile's weight slab 2-4 groups ahead (4-byte copies
 // into a dummy LDS area) made all three 10-13 % slower and was dropped.
-// Balancing the real tiles over the 8 XCDs (FP8BLK_GROUPED_BALANCE, in place
-// of a remap over the whole upper-bound grid, which left the MoE shapes'
-// tiles to six XCDs, 1.27x the balanced share on the busiest): MoE up 3.35 ->
+// Balancing the real tiles over the 8 XCDs (k_grouped_gemm, in place of a
+// remap over the whole upper-bound grid, which left the MoE shapes' tiles to
+// six XCDs, 1.27x the balanced share on the busiest): MoE up 3.35 ->
 // 2.94 ms, down 2.15 -> 1.81 ms, down Dgrad 1.72 -> 1.45 ms (interleaved, one
 // box, bitwise identical), so a grouped tile now takes within a few percent of
 // a dense tile's time (2.94 ms over 25.2 tiles per CU).
 #ifndef FP8BLK_GROUPED_SKIP
 #define FP8BLK_GROUPED_SKIP 1
-#endif
-#ifndef FP8BLK_GROUPED_BALANCE
-#define FP8BLK_GROUPED_BALANCE 1
 #endif
 #ifndef FP8BLK_GROUPED_REG_CHUNKS
 #define FP8BLK_GROUPED_REG_CHUNKS 4
@@ -1193,7 +1190,6 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
     for (int64_t e0 = 0; e0 < G; e0 += 64)
       total = wave_uniform(total + __shfl(wave_inclusive_sum(expert_tiles(e0 + lane)), 63));
   }
-#if FP8BLK_GROUPED_BALANCE
   // Workgroups are dealt to the 8 XCDs round-robin: workgroup b runs on XCD
   // b % 8, as that XCD's (b / 8)-th.  XCD x takes the contiguous run
   // [x * per, (x + 1) * per) of the `total` real tiles, so that the XCDs get
@@ -1205,11 +1201,6 @@ __global__ __launch_bounds__(CFG::NT) void k_grouped_gemm(int64_t G, const int32
   if (slot >= per) return;  // surplus workgroup (uniform across the block)
   const int64_t lin = (int64_t)(blockIdx.x % 8) * per + slot;
   if (lin >= total) return;
-#else
-  const int64_t nblocks = gridDim.x;
-  int64_t lin = blockIdx.x;
-  if (nblocks % 8 == 0) lin = (lin % 8) * (nblocks / 8) + lin / 8;
-#endif
 
   int64_t e = -1, local = 0;
   if (in_regs) {
