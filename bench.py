@@ -49,8 +49,8 @@ QUANT_BYTES_BLOCK = 2 + 1 + 4 / (128 * 128)
 # of its 4 x 8 block of tiles once (8 x 12 x 1.84 MB); sharing across XCDs is
 # left to the Infinity Cache.  Valid only for the GEMM source it was measured
 # on (sha256 below); reported as null otherwise.
-GEMM_TRAFFIC = {"sha256": "6808d9f0f5e29a5f8c6b7458421750ba9d6a9666d086441eaaa234236e045790",
-                "fetch_bytes": 178243183, "write_bytes": 67108978}
+GEMM_TRAFFIC = {"sha256": "d7ab41e494250c7fa40bd673b214cd9b1e704c79ec03b43732dabd4a11643264",
+                "fetch_bytes": 178243156, "write_bytes": 67108864}
 
 
 def parse():
