@@ -43,6 +43,12 @@ def test_grouped_small(opB, counts):
     Cg = np_f32(C)
     if Mt == 0:
         return
+    # the caller's bound on any expert's rows sizes the grid from it (here
+    # often the tighter bound): the same result
+    Cm = fb.grouped_gemm_fp8_blockscaled(offs, u8_dev(qA), f32_dev(sA), u8_dev(B), f32_dev(sB), opB=opB,
+                                         max_group_rows=max(counts))
+    torch.cuda.synchronize()
+    assert np.array_equal(np_f32(Cm).view(np.uint32), Cg.view(np.uint32))
     R = oracle.grouped_gemm_blockscaled(off, qA, sA, B, sB, opB)
     assert e_norm(Cg, R) <= 1e-3
     for e in range(len(counts)):
@@ -77,8 +83,11 @@ def test_grouped_many_experts(G):
     sB = sW.reshape(G, K // 128, -1)
     offs = torch.from_numpy(off.astype(np.int32)).cuda()
     C = fb.grouped_gemm_fp8_blockscaled(offs, u8_dev(qA), f32_dev(sA), u8_dev(B), f32_dev(sB))
+    Cm = fb.grouped_gemm_fp8_blockscaled(offs, u8_dev(qA), f32_dev(sA), u8_dev(B), f32_dev(sB),
+                                         max_group_rows=int(counts.max()))
     torch.cuda.synchronize()
     Cg = np_f32(C)
+    assert np.array_equal(np_f32(Cm).view(np.uint32), Cg.view(np.uint32))
     R = oracle.grouped_gemm_blockscaled(off, qA, sA, B, sB, oracle.OP_N)
     assert e_norm(Cg, R) <= 1e-3
     dA, dsA = u8_dev(qA), f32_dev(sA)
